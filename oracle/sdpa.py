@@ -1,0 +1,231 @@
+"""CPU oracle for grouped-query prefill attention (fp64, explicit mask).
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or execute this module; it is
+used by the test-suite, by ``__graft_entry__.smoke()`` and by the CPU-baseline leg of ``bench.py``.
+It shares no code with the HIP library: it reads the same seeded bf16 input bits, widens them to
+fp64 itself and computes the plain definition of masked scaled-dot-product attention. The online
+(streaming) softmax of the tiled method is an exact reformulation of that definition (tiny-llm,
+Week 2 Day 5 "Tiled Dense Prefill Attention", Task 1, the merge equations), so the oracle is the
+definition written out, not a replay of the tiles.
+
+Definition implemented (one batch element b, one query head h):
+
+* KV head: ``hk = floor(h / (Hq / Hkv))`` -- tiny-llm Week 2 Day 5, Task 1 (layout contract).
+* Visibility of key j for query row i (``vis``), every term optional:
+    - causal, aligned to the end of the cached prefix: ``j <= i + causal_offset``
+      (tinygrad "symbolic llm with prefill": the prefill mask is the lower-right triangle
+      ``full(-inf).triu(start_pos + 1)``; tiny-llm Task 2: row i sees through ``S - L + i``);
+    - sliding window of W keys including the row's own position:
+      ``j >= i + causal_offset - W + 1`` (TensorFold PR "What changes": the mask term
+      ``col < row - WINDOW + 1``; brotensor ``flash_attention_windowed_forward``: keys
+      ``[max(0, pos - window + 1), pos]``, window <= 0 unbounded);
+    - key padding: ``key_mask[b, j] != 0`` (brotensor ``flash_attention_gqa_forward``: a
+      length-Lk key mask, valid / invalid);
+    - always ``j < S``.
+* ``A[i, j] = 0`` if vis else ``-inf``; ``scores = scale * Q K^T + A``;
+  ``O[i] = softmax(scores[i]) V``.
+* A row with no visible key has no probability mass and its output is all zeros
+  (tiny-llm Task 2).
+
+Readings taken where the pages leave a step open: ``causal_offset < 0`` means no causal term;
+a window needs the causal term; the key mask is ``uint8`` with nonzero meaning valid.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+NO_CAUSAL = -1
+
+
+# ----------------------------------------------------------------------------------------------
+# Input widening (bf16 bits -> exact fp64)
+# ----------------------------------------------------------------------------------------------
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to fp64 exactly: a bf16 is the top half of a float32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------------------------
+# Head map and mask (kept as separate functions so the tests can plant mistakes in them)
+# ----------------------------------------------------------------------------------------------
+def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
+    """Query head h reads KV head floor(h / (Hq / Hkv)) (tiny-llm Week 2 Day 5, Task 1)."""
+    group = Hq // Hkv
+    return h // group
+
+
+def visible(rows: np.ndarray, S: int, causal_offset: int, window: int,
+            key_valid: np.ndarray | None) -> np.ndarray:
+    """Boolean [len(rows), S]: may query row i attend key j.
+
+    Causal term (lower-right): j <= i + causal_offset, applied when causal_offset >= 0
+    (tinygrad prefill mask; tiny-llm Task 2). Window term: j >= i + causal_offset - window + 1
+    when window > 0 (TensorFold mask term; brotensor windowed forward). Key term:
+    key_valid[j] (brotensor key mask)."""
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(S, dtype=np.int64)[None, :]
+    vis = np.ones((i.shape[0], S), dtype=bool)
+    if causal_offset >= 0:
+        vis &= j <= i + causal_offset
+        if window > 0:
+            vis &= j >= i + causal_offset - window + 1
+    if key_valid is not None:
+        vis &= np.asarray(key_valid, dtype=bool)[None, :]
+    return vis
+
+
+def additive_mask(rows: np.ndarray, S: int, causal_offset: int, window: int,
+                  key_valid: np.ndarray | None) -> np.ndarray:
+    """The explicit additive mask: 0 where visible, -inf elsewhere (fp64)."""
+    vis = visible(rows, S, causal_offset, window, key_valid)
+    return np.where(vis, 0.0, -np.inf)
+
+
+def check_args(B, Hq, Hkv, L, S, D, causal_offset, window):
+    if min(B, Hq, Hkv, L, S, D) < 1:
+        raise ValueError("all sizes must be >= 1")
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if window > 0 and causal_offset < 0:
+        raise ValueError("a sliding window needs the causal term")
+
+
+# ----------------------------------------------------------------------------------------------
+# The oracle proper
+# ----------------------------------------------------------------------------------------------
+def _softmax_rows_times_v(scores: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Plain softmax over each row of `scores` (with -inf entries), times v. Empty rows -> 0."""
+    m = np.max(scores, axis=1, keepdims=True)
+    empty = ~np.isfinite(m[:, 0])
+    m = np.where(np.isfinite(m), m, 0.0)
+    p = np.exp(scores - m)          # exp(-inf) = 0 exactly
+    l = np.sum(p, axis=1, keepdims=True)
+    out = (p @ v) / np.where(l > 0, l, 1.0)
+    out[empty] = 0.0
+    return out
+
+
+def attention_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.ndarray,
+                   scale: float, causal_offset: int, window: int,
+                   key_valid: np.ndarray | None) -> np.ndarray:
+    """Output rows for one (b, h): q_rows [n, D] at query positions `rows`, k/v [S, D] (fp64)."""
+    S = k.shape[0]
+    scores = float(scale) * (q_rows @ k.T)
+    scores = scores + additive_mask(rows, S, causal_offset, window, key_valid)
+    return _softmax_rows_times_v(scores, v)
+
+
+def _widen(x):
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f64(x)
+    return np.asarray(x, dtype=np.float64)
+
+
+def oracle_sdpa(q, k, v, scale, causal_offset: int = NO_CAUSAL, window: int = 0,
+                key_mask: np.ndarray | None = None, row_block: int = 256,
+                workers: int = 1) -> np.ndarray:
+    """Masked grouped-query SDPA in fp64.
+
+    q: [B,Hq,L,D], k/v: [B,Hkv,S,D] as bf16 bits (uint16) or floats; key_mask: uint8 [B,S] or
+    None. Returns fp64 [B,Hq,L,D]. Rows are processed in blocks of `row_block` to bound memory;
+    `workers` > 1 spreads (b, h, row block) items over a thread pool (numpy releases the GIL)."""
+    q, k, v = _widen(q), _widen(k), _widen(v)
+    B, Hq, L, D = q.shape
+    _, Hkv, S, _ = k.shape
+    check_args(B, Hq, Hkv, L, S, D, causal_offset, window)
+    out = np.zeros((B, Hq, L, v.shape[-1]), dtype=np.float64)
+    scale = float(np.float64(scale))
+    items = [(b, h, r0) for b in range(B) for h in range(Hq) for r0 in range(0, L, row_block)]
+
+    def run(item):
+        b, h, r0 = item
+        hk = kv_head_of(h, Hq, Hkv)
+        rows = np.arange(r0, min(r0 + row_block, L))
+        kv = None if key_mask is None else (key_mask[b] != 0)
+        out[b, h, rows] = attention_rows(q[b, h, rows], k[b, hk], v[b, hk], rows, scale,
+                                         causal_offset, window, kv)
+
+    if workers <= 1:
+        for it in items:
+            run(it)
+    else:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(run, items))
+    return out
+
+
+def oracle_selected_rows(q, k, v, scale, causal_offset, window, key_mask, picks) -> np.ndarray:
+    """Oracle output for selected (b, h, row) triples only: returns fp64 [len(picks), D].
+
+    Used at full workload sizes, where computing every row would take too long."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    res = []
+    for (b, h, i) in picks:
+        hk = kv_head_of(h, Hq, Hkv)
+        kb, vb = _widen(k[b, hk]), _widen(v[b, hk])
+        qr = _widen(q[b, h, i:i + 1])
+        kv = None if key_mask is None else (key_mask[b] != 0)
+        res.append(attention_rows(qr, kb, vb, np.array([i]), float(np.float64(scale)),
+                                  causal_offset, window, kv)[0])
+    return np.array(res)
+
+
+def visible_pair_count(B, Hq, L, S, causal_offset, window, key_mask=None, row_block=1024) -> int:
+    """Number of visible (query row, key) cells summed over all query heads, by building the
+    explicit mask row block by row block."""
+    total = 0
+    for b in range(B):
+        kv = None if key_mask is None else (key_mask[b] != 0)
+        for r0 in range(0, L, row_block):
+            rows = np.arange(r0, min(r0 + row_block, L))
+            total += int(np.count_nonzero(visible(rows, S, causal_offset, window, kv)))
+    return total * Hq
+
+
+# ----------------------------------------------------------------------------------------------
+# Brute force (pure Python scalars) for tiny cases
+# ----------------------------------------------------------------------------------------------
+def brute_sdpa(q, k, v, scale, causal_offset=NO_CAUSAL, window=0, key_mask=None):
+    """Scalar-loop SDPA on nested lists / small arrays, with math.exp. Shapes as oracle_sdpa."""
+    q, k, v = _widen(np.asarray(q)), _widen(np.asarray(k)), _widen(np.asarray(v))
+    B, Hq, L, D = q.shape
+    Hkv, S, Dv = k.shape[1], k.shape[2], v.shape[3]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, L, Dv))
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // G
+            for i in range(L):
+                keys = []
+                for j in range(S):
+                    if causal_offset >= 0 and j > i + causal_offset:
+                        continue
+                    if causal_offset >= 0 and window > 0 and j < i + causal_offset - window + 1:
+                        continue
+                    if key_mask is not None and not key_mask[b][j]:
+                        continue
+                    s = 0.0
+                    for d in range(D):
+                        s += float(q[b, h, i, d]) * float(k[b, hk, j, d])
+                    keys.append((j, float(scale) * s))
+                if not keys:
+                    continue
+                mx = max(s for _, s in keys)
+                w = [(j, math.exp(s - mx)) for j, s in keys]
+                tot = sum(x for _, x in w)
+                for d in range(Dv):
+                    out[b, h, i, d] = sum(x * float(v[b, hk, j, d]) for j, x in w) / tot
+    return out
+
+
+def host_workers() -> int:
+    """Threads the oracle's timing mode uses: the cores in this process's affinity mask."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1

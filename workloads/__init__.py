@@ -1,0 +1,101 @@
+"""Seeded synthetic workloads for grouped-query prefill attention.
+
+This module is shared by the HIP path's tests and bench and by the CPU oracle. It holds no attention
+arithmetic: only the table of workload shapes and mask arguments, and the generator of the bf16 input
+bits that both sides consume. The GPU receives the bits through a bf16 view; the oracle widens the
+same bits to fp64 by itself.
+
+Workload recipe (shapes from the pages' workloads, values synthetic):
+
+* Q, K, V are drawn as float32 standard normals from ``numpy.random.default_rng(seed)`` in the
+  order Q, K, V, then (only for the key-padding workload) the per-sequence valid lengths.
+* An amplitude factor (a power of two, so exact) scales the draws; the small prompt case uses 0.5.
+* Each float32 is rounded to bf16 with round-to-nearest-even on its bit pattern.
+* ``scale`` is the float32 value of ``1/sqrt(D)``, handed to both sides unchanged.
+* Key padding: ``key_mask[b, j] = 1`` for ``j < n_b`` with ``n_b`` drawn uniformly from the
+  integers 1024..4096 inclusive.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NO_CAUSAL = -1
+
+# name -> workload.  `causal_offset` < 0 means no causal mask (bidirectional).
+CONFIGS: dict[str, dict] = {
+    # tiny-llm Week 2 Day 5, Task 1: the causal GQA witness, 33 query rows over 47 keys.
+    "causal_witness_33x47": dict(B=1, Hq=4, Hkv=2, D=128, L=33, S=47, causal_offset=14, window=0,
+                                 amp=1.0, key_padding=None),
+    # Small-model prompt prefill, L = S = 128, inputs scaled by 0.5.
+    "small_prompt_128": dict(B=1, Hq=16, Hkv=8, D=128, L=128, S=128, causal_offset=0, window=0,
+                             amp=0.5, key_padding=None),
+    # Mid-context chunk: 2048 new rows on a 6144-key prefix, Llama-style G = 7 grouping
+    # (TensorFold PR, geometry DH 128, NQ 56, G 7, KVH 8).
+    "mid_ctx_8k": dict(B=1, Hq=56, Hkv=8, D=128, L=2048, S=8192, causal_offset=6144, window=0,
+                       amp=1.0, key_padding=None),
+    # Sliding-window chunk on a rotating cache of W - 1 + L keys (mlx-lm PR, commit text).
+    "sliding_w1024_d128": dict(B=1, Hq=32, Hkv=8, D=128, L=2048, S=3071, causal_offset=1023,
+                               window=1024, amp=1.0, key_padding=None),
+    "sliding_w1024_d64": dict(B=1, Hq=32, Hkv=8, D=64, L=2048, S=3071, causal_offset=1023,
+                              window=1024, amp=1.0, key_padding=None),
+    # Long-context chunk: 2048 new rows on a 30720-key prefix.
+    "long_ctx_32k": dict(B=1, Hq=32, Hkv=8, D=128, L=2048, S=32768, causal_offset=30720, window=0,
+                         amp=1.0, key_padding=None),
+    # Batched bidirectional prefill with per-sequence key padding (encoder-style prefill).
+    "bidir_padded_b8": dict(B=8, Hq=32, Hkv=8, D=128, L=4096, S=4096, causal_offset=NO_CAUSAL,
+                            window=0, amp=1.0, key_padding=(1024, 4096)),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even) and return the uint16 bits.
+
+    Inputs must be finite (the generators never produce NaN or infinity)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def make_inputs(cfg: dict | str, seed: int = 0, **overrides) -> dict:
+    """Draw one workload's inputs.
+
+    Returns a dict with ``q``, ``k``, ``v`` (uint16 bf16 bit arrays of shapes [B,Hq,L,D],
+    [B,Hkv,S,D], [B,Hkv,S,D]), ``key_mask`` (uint8 [B,S] or None), ``key_lengths`` (or None),
+    ``scale`` (numpy float32) and the shape/mask arguments.
+    """
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    c = dict(cfg)
+    c.update(overrides)
+    B, Hq, Hkv, D, L, S = (int(c[n]) for n in ("B", "Hq", "Hkv", "D", "L", "S"))
+    amp = np.float32(c.get("amp", 1.0))
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, L, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    if amp != 1.0:
+        q *= amp
+        k *= amp
+        v *= amp
+    key_mask = None
+    lengths = None
+    kp = c.get("key_padding")
+    if kp is not None:
+        lo, hi = kp
+        lengths = rng.integers(lo, hi + 1, size=B)
+        key_mask = (np.arange(S)[None, :] < lengths[:, None]).astype(np.uint8)
+    return dict(
+        q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k), v=f32_to_bf16_bits(v),
+        key_mask=key_mask, key_lengths=lengths,
+        scale=np.float32(1.0 / np.sqrt(np.float32(D))) if c.get("scale") is None else np.float32(c["scale"]),
+        B=B, Hq=Hq, Hkv=Hkv, D=D, L=L, S=S,
+        causal_offset=int(c.get("causal_offset", NO_CAUSAL)), window=int(c.get("window", 0)),
+    )
+
+
+def random_bits(rng: np.random.Generator, shape, amp: float = 1.0) -> np.ndarray:
+    """bf16 bits of amp * N(0,1) float32 draws from an existing generator."""
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if amp != 1.0:
+        x *= np.float32(amp)
+    return f32_to_bf16_bits(x)
