@@ -1,0 +1,117 @@
+/*
+ * pfa.h -- C ABI of the gfx950 (MI355X) grouped-query flash prefill attention library.
+ *
+ * One operation: masked scaled-dot-product attention for a prefill chunk of L new query rows
+ * against S keys that include a cached prefix, with grouped-query heads.
+ *
+ *   O[b,h,i,:] = sum_j softmax_j( scale * Q[b,h,i,:] . K[b,hk,j,:] + A[b,i,j] ) * V[b,hk,j,:]
+ *   hk = floor(h / (Hq / Hkv))
+ *
+ * Sources for the definition (page titles and sections):
+ *  - tiny-llm, Week 2 Day 5 "Tiled Dense Prefill Attention", Task 1: the layout contract
+ *    Q [B,Hq,L,D], K/V [B,Hkv,S,D], output [B,Hq,L,D]; Hq % Hkv == 0; query head h reads KV head
+ *    floor(h / (Hq/Hkv)) without copying K/V into Hq heads; FP32 running max / sum / accumulator
+ *    merged tile by tile (the merge equations); BF16 only after the final FP32 normalisation.
+ *  - same page, Task 2: causality aligned to the end of the cached prefix (row i sees keys through
+ *    S - L + i); a row with no visible key returns finite zeros; tiles with no valid score skipped.
+ *  - tinygrad "symbolic llm with prefill": the prefill mask is the lower-right triangle
+ *    full(-inf).triu(start_pos + 1), not the upper-left one of is_causal.
+ *  - TensorFold PR "Spark2.5's and Llama's prompt attention from one source", "What changes": the
+ *    sliding-window mask term col < row - WINDOW + 1 and the window's first key block.
+ *  - brotensor flash_attention.h: flash_attention_windowed_forward (query at absolute position
+ *    pos sees keys [max(0, pos - window + 1), pos]; window <= 0 unbounded),
+ *    flash_attention_gqa_forward (causal or bidirectional, length-Lk key mask), and
+ *    flash_attention_decode_masked (fully masked key tiles skipped without touching K/V, result
+ *    bit-identical to the unmasked call).
+ *  - mlx-lm PR "Skip fully masked key tiles in Flint sliding-window prefill": skipping must keep
+ *    the kernel's key-tile grid, so the result is bit-identical to visiting every tile; the
+ *    window is an explicit argument, never inferred from a mask.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, contiguous, row-major,
+ *    owned by the caller. The library never allocates, frees or copies device memory and keeps no
+ *    global mutable state; calls are thread-safe.
+ *  - Arguments are validated on the host before anything is enqueued; on any error nothing is
+ *    launched and O is left untouched.
+ *  - Success means the kernel was enqueued on `stream` (asynchronous; no host synchronisation).
+ */
+#ifndef PFA_H
+#define PFA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PFA_VERSION 10000 /* 1.0.0 */
+
+/* causal_offset < 0 selects bidirectional attention (no causal term). */
+#define PFA_NO_CAUSAL (-1)
+
+/* Visit every key tile of the grid and mask elementwise instead of skipping fully masked tiles.
+ * Exists for the bit-identity check: the result must equal the default (skipping) call bit for
+ * bit. */
+#define PFA_FLAG_NO_SKIP 1u
+
+enum pfa_status {
+  PFA_OK = 0,
+  PFA_ERR_NULL = 1,      /* Q, K, V or O is NULL                                               */
+  PFA_ERR_SIZE = 2,      /* a size < 1, or a size product / launch grid does not fit            */
+  PFA_ERR_GQA = 3,       /* Hq is not a multiple of Hkv                                         */
+  PFA_ERR_HEAD_DIM = 4,  /* D is not 64 or 128                                                  */
+  PFA_ERR_MASK_ARGS = 5, /* window > 0 without the causal term                                  */
+  PFA_ERR_SCALE = 6,     /* scale is not finite or not > 0                                      */
+  PFA_ERR_ALIGN = 7,     /* Q, K, V or O is not 16-byte aligned                                 */
+  PFA_ERR_ALIAS = 8,     /* O overlaps Q, K, V or key_mask                                      */
+  PFA_ERR_FLAGS = 9,     /* unknown bit in flags                                                */
+  PFA_ERR_LAUNCH = 10    /* the HIP launch failed (e.g. no gfx950 device is current)            */
+};
+
+/*
+ * prefill_attn_gqa -- grouped-query flash prefill attention, BF16 in / BF16 out, FP32 softmax.
+ *
+ *   Q            bf16 [B, Hq,  L, D]   queries of the new chunk
+ *   K, V         bf16 [B, Hkv, S, D]   keys / values, S includes the cached prefix
+ *   B            batch size (>= 1)
+ *   Hq, Hkv      query heads and KV heads (>= 1, Hq % Hkv == 0; Hq == Hkv is plain MHA)
+ *   L, S         query rows and keys (>= 1; any combination, L > S allowed)
+ *   D            head dimension, 64 or 128
+ *   scale        score scale, finite and > 0 (usually 1/sqrt(D)); applied to Q.K^T in FP32
+ *   causal_offset  >= 0: row i sees keys j <= i + causal_offset (S - L for a prefill chunk);
+ *                  < 0 (PFA_NO_CAUSAL): no causal term (bidirectional)
+ *   window       > 0: row i also needs j >= i + causal_offset - window + 1 (window keys including
+ *                its own position); requires causal_offset >= 0. <= 0: no window term
+ *   key_mask     NULL, or uint8 [B, S]: nonzero = key valid, 0 = key dropped for every row of that
+ *                batch element. No alignment requirement
+ *   O            bf16 [B, Hq, L, D], fully overwritten; rows with no visible key are set to 0
+ *   stream       hipStream_t to enqueue on; NULL = the default stream
+ *
+ * Keys are always limited to j < S. Fully masked key tiles are skipped before their K/V tile is
+ * loaded; the result is bit-identical to prefill_attn_gqa_ex(..., PFA_FLAG_NO_SKIP).
+ * Returns a pfa_status code.
+ */
+int prefill_attn_gqa(const void* Q, const void* K, const void* V,
+                     int B, int Hq, int Hkv, int L, int S, int D,
+                     float scale, int causal_offset, int window,
+                     const uint8_t* key_mask, void* O, void* stream);
+
+/* As prefill_attn_gqa, with a flags word (0 or PFA_FLAG_NO_SKIP).
+ * prefill_attn_gqa(...) == prefill_attn_gqa_ex(..., 0). */
+int prefill_attn_gqa_ex(const void* Q, const void* K, const void* V,
+                        int B, int Hq, int Hkv, int L, int S, int D,
+                        float scale, int causal_offset, int window,
+                        const uint8_t* key_mask, void* O, void* stream,
+                        unsigned flags);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* pfa_status_str(int status);
+
+/* PFA_VERSION of the built library. */
+int pfa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PFA_H */

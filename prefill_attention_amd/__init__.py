@@ -1,0 +1,17 @@
+"""Grouped-query flash prefill attention for AMD Instinct MI355X (gfx950).
+
+The computation runs in ``libpfa.so`` (hand-written HIP); this package is its thin Python binding.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    FLAG_NO_SKIP,
+    LIB_PATH,
+    NO_CAUSAL,
+    STATUS,
+    PfaError,
+    library,
+    prefill_attn_gqa,
+    prefill_attn_gqa_raw,
+    status_str,
+    version,
+)

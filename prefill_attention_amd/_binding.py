@@ -1,0 +1,143 @@
+"""ctypes binding of libpfa.so: argument marshalling only.
+
+Every step of the attention runs in the HIP library; this module checks tensor metadata, reads
+device pointers and the current stream from torch, and forwards them to the C ABI. There is no
+fallback path: if the library is missing or the call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpfa.so")
+
+# Mirrors of include/pfa.h
+NO_CAUSAL = -1
+FLAG_NO_SKIP = 1
+STATUS = {
+    0: "PFA_OK", 1: "PFA_ERR_NULL", 2: "PFA_ERR_SIZE", 3: "PFA_ERR_GQA", 4: "PFA_ERR_HEAD_DIM",
+    5: "PFA_ERR_MASK_ARGS", 6: "PFA_ERR_SCALE", 7: "PFA_ERR_ALIGN", 8: "PFA_ERR_ALIAS",
+    9: "PFA_ERR_FLAGS", 10: "PFA_ERR_LAUNCH",
+}
+EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "pfa_status_str", "pfa_version")
+
+_lib = None
+
+
+class PfaError(RuntimeError):
+    """A nonzero status from the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """Load libpfa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m prefill_attention_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, ci, cf, cu = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint
+        sig = [vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp, vp, vp]
+        lib.prefill_attn_gqa.argtypes = sig
+        lib.prefill_attn_gqa.restype = ci
+        lib.prefill_attn_gqa_ex.argtypes = sig + [cu]
+        lib.prefill_attn_gqa_ex.restype = ci
+        lib.pfa_status_str.argtypes = [ci]
+        lib.pfa_status_str.restype = ctypes.c_char_p
+        lib.pfa_version.argtypes = []
+        lib.pfa_version.restype = ci
+        _lib = lib
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return library().pfa_status_str(int(status)).decode()
+
+
+def version() -> int:
+    return int(library().pfa_version())
+
+
+def prefill_attn_gqa_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: int, Hkv: int, L: int,
+                         S: int, D: int, scale: float, causal_offset: int, window: int,
+                         key_mask_ptr: int | None, o_ptr: int, stream: int | None,
+                         flags: int = 0) -> int:
+    """Direct C-ABI call with integer pointers; returns the status code."""
+    return int(library().prefill_attn_gqa_ex(
+        q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
+        key_mask_ptr or None, o_ptr, stream or None, flags))
+
+
+def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True,
+                     causal_offset: int | None = None, window: int = 0, key_mask=None, out=None,
+                     no_skip: bool = False, stream=None):
+    """Grouped-query prefill attention on torch tensors.
+
+    q: bf16 [B,Hq,L,D]; k, v: bf16 [B,Hkv,S,D]; key_mask: optional uint8/bool [B,S] (nonzero =
+    valid). scale defaults to 1/sqrt(D). With causal=True the causal offset defaults to S - L
+    (the chunk is the tail of the S keys); causal=False is bidirectional. window > 0 adds a
+    sliding window of that many keys. Returns `out` (allocated if None), bf16 [B,Hq,L,D].
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+    B, Hq, L, D = q.shape
+    Bk, Hkv, S, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k and v shapes differ: {tuple(k.shape)} vs {tuple(v.shape)}")
+    if Bk != B or Dk != D:
+        raise ValueError(f"batch / head dim mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if causal:
+        if causal_offset is None:
+            causal_offset = S - L
+        if causal_offset < 0:
+            raise ValueError(f"causal attention needs causal_offset >= 0 (got {causal_offset})")
+    else:
+        if causal_offset is not None and causal_offset >= 0:
+            raise ValueError("causal=False takes no causal_offset")
+        if window > 0:
+            raise ValueError("a sliding window needs causal=True")
+        causal_offset = NO_CAUSAL
+    mask_ptr = None
+    if key_mask is not None:
+        if key_mask.dtype == torch.bool:
+            key_mask = key_mask.view(torch.uint8)
+        if key_mask.dtype != torch.uint8:
+            raise ValueError("key_mask must be uint8 or bool")
+        if tuple(key_mask.shape) != (B, S) or key_mask.device != q.device or not key_mask.is_contiguous():
+            raise ValueError(f"key_mask must be a contiguous [B,S]=({B},{S}) tensor on {q.device}")
+        mask_ptr = key_mask.data_ptr()
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    stream_ptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        rc = prefill_attn_gqa_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
+                                  float(scale), int(causal_offset), int(window), mask_ptr,
+                                  out.data_ptr(), stream_ptr, FLAG_NO_SKIP if no_skip else 0)
+    if rc != 0:
+        raise PfaError(rc, status_str(rc))
+    return out

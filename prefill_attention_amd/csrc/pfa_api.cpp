@@ -1,0 +1,123 @@
+// C-ABI entry points: argument validation (host only, before anything is enqueued) and dispatch
+// to the HIP launcher. This file uses no HIP API, so its checks run without a GPU.
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/pfa.h"
+#include "pfa_internal.h"
+
+namespace {
+
+bool mul_fits(long long a, long long b, long long limit, long long* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > limit / a) return false;
+  *out = a * b;
+  return true;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int validate(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L, int S,
+             int D, float scale, int causal_offset, int window, const uint8_t* key_mask,
+             void* O, unsigned flags) {
+  if (!Q || !K || !V || !O) return PFA_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || S < 1 || D < 1) return PFA_ERR_SIZE;
+  // Element counts must fit comfortably in 64 bits; byte offsets are formed in 64 bits.
+  const long long lim = LLONG_MAX / 4;
+  long long q_elems, kv_elems, t;
+  if (!mul_fits(B, Hq, lim, &t) || !mul_fits(t, L, lim, &t) || !mul_fits(t, D, lim, &q_elems))
+    return PFA_ERR_SIZE;
+  if (!mul_fits(B, Hkv, lim, &t) || !mul_fits(t, S, lim, &t) || !mul_fits(t, D, lim, &kv_elems))
+    return PFA_ERR_SIZE;
+  // Row/key coordinates are compared as i + causal_offset in 64-bit, so any int is fine there.
+  if (Hq % Hkv != 0) return PFA_ERR_GQA;
+  if (D != 64 && D != 128) return PFA_ERR_HEAD_DIM;
+  if (window > 0 && causal_offset < 0) return PFA_ERR_MASK_ARGS;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return PFA_ERR_SCALE;
+  const uintptr_t a16 = 15;
+  if ((reinterpret_cast<uintptr_t>(Q) & a16) || (reinterpret_cast<uintptr_t>(K) & a16) ||
+      (reinterpret_cast<uintptr_t>(V) & a16) || (reinterpret_cast<uintptr_t>(O) & a16))
+    return PFA_ERR_ALIGN;
+  const Range o{reinterpret_cast<uintptr_t>(O),
+                reinterpret_cast<uintptr_t>(O) + static_cast<uintptr_t>(q_elems) * 2u};
+  const Range rq{reinterpret_cast<uintptr_t>(Q),
+                 reinterpret_cast<uintptr_t>(Q) + static_cast<uintptr_t>(q_elems) * 2u};
+  const Range rk{reinterpret_cast<uintptr_t>(K),
+                 reinterpret_cast<uintptr_t>(K) + static_cast<uintptr_t>(kv_elems) * 2u};
+  const Range rv{reinterpret_cast<uintptr_t>(V),
+                 reinterpret_cast<uintptr_t>(V) + static_cast<uintptr_t>(kv_elems) * 2u};
+  if (overlaps(o, rq) || overlaps(o, rk) || overlaps(o, rv)) return PFA_ERR_ALIAS;
+  if (key_mask) {
+    const Range rm{reinterpret_cast<uintptr_t>(key_mask),
+                   reinterpret_cast<uintptr_t>(key_mask) +
+                       static_cast<uintptr_t>(B) * static_cast<uintptr_t>(S)};
+    if (overlaps(o, rm)) return PFA_ERR_ALIAS;
+  }
+  if (flags & ~PFA_FLAG_NO_SKIP) return PFA_ERR_FLAGS;
+  return PFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int prefill_attn_gqa_ex(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv,
+                        int L, int S, int D, float scale, int causal_offset, int window,
+                        const uint8_t* key_mask, void* O, void* stream, unsigned flags) {
+  int rc = validate(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window, key_mask, O,
+                    flags);
+  if (rc != PFA_OK) return rc;
+  pfa::Launch p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.key_mask = key_mask;
+  p.o = O;
+  p.batch = B;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.group = Hq / Hkv;
+  p.lq = L;
+  p.sk = S;
+  p.d = D;
+  p.scale = scale;
+  p.causal_offset = causal_offset < 0 ? PFA_NO_CAUSAL : causal_offset;
+  p.window = (causal_offset >= 0 && window > 0) ? window : 0;
+  p.flags = flags;
+  p.stream = stream;
+  if (pfa::grid_blocks(p) > INT_MAX) return PFA_ERR_SIZE;
+  return pfa::launch_prefill(p);
+}
+
+int prefill_attn_gqa(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L,
+                     int S, int D, float scale, int causal_offset, int window,
+                     const uint8_t* key_mask, void* O, void* stream) {
+  return prefill_attn_gqa_ex(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window,
+                             key_mask, O, stream, 0u);
+}
+
+const char* pfa_status_str(int status) {
+  switch (status) {
+    case PFA_OK: return "ok";
+    case PFA_ERR_NULL: return "null tensor pointer (Q, K, V and O are required)";
+    case PFA_ERR_SIZE: return "invalid size: B, Hq, Hkv, L, S, D must be >= 1 and fit the launch";
+    case PFA_ERR_GQA: return "Hq must be a multiple of Hkv";
+    case PFA_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
+    case PFA_ERR_MASK_ARGS: return "a sliding window (window > 0) requires causal_offset >= 0";
+    case PFA_ERR_SCALE: return "scale must be finite and > 0";
+    case PFA_ERR_ALIGN: return "Q, K, V and O must be 16-byte aligned";
+    case PFA_ERR_ALIAS: return "O must not overlap Q, K, V or key_mask";
+    case PFA_ERR_FLAGS: return "unknown flag bit";
+    case PFA_ERR_LAUNCH: return "HIP kernel launch failed (is a gfx950 device current?)";
+    default: return "unknown status";
+  }
+}
+
+int pfa_version(void) { return PFA_VERSION; }
+
+}  // extern "C"

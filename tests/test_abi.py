@@ -1,0 +1,130 @@
+"""C-ABI tests that need no GPU: the library loads, exports what include/pfa.h declares, and every
+invalid argument is rejected on the host with its status code before anything is launched."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import prefill_attention_amd as pfa
+from prefill_attention_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pfa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pfa.LIB_PATH):
+        from prefill_attention_amd.build import build_library
+        build_library()
+    return pfa.library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def header_defines():
+    text = open(HEADER).read()
+    vals = dict(re.findall(r"#define\s+(PFA_\w+)\s+\(?(-?\d+)u?\)?", text))
+    enum = dict(re.findall(r"(PFA_(?:OK|ERR_\w+))\s*=\s*(\d+)", text))
+    return {k: int(v) for k, v in vals.items()}, {k: int(v) for k, v in enum.items()}
+
+
+def test_exports_every_declared_symbol(lib):
+    funcs = header_functions()
+    assert set(funcs) == set(pfa.EXPORTS), funcs
+    for name in funcs:
+        assert hasattr(lib, name), name
+
+
+def test_binding_constants_match_header(lib):
+    defines, enum = header_defines()
+    assert defines["PFA_NO_CAUSAL"] == pfa.NO_CAUSAL
+    assert defines["PFA_FLAG_NO_SKIP"] == pfa.FLAG_NO_SKIP
+    assert defines["PFA_VERSION"] == pfa.version()
+    assert {v: k for k, v in enum.items()} == pfa.STATUS
+
+
+def test_status_strings(lib):
+    for code in list(pfa.STATUS) + [99, -1]:
+        s = pfa.status_str(code)
+        assert isinstance(s, str) and s
+    assert pfa.status_str(0) == "ok"
+    assert pfa.status_str(99) == "unknown status"
+
+
+# Fake, 16-byte aligned, non-overlapping "device" addresses: validation never dereferences them and
+# returns before any HIP call when an argument is invalid.
+A = 1 << 40
+Q, K, V, O, M = A, 2 * A, 3 * A, 4 * A, 5 * A
+GOOD = dict(q=Q, k=K, v=V, B=1, Hq=4, Hkv=2, L=33, S=47, D=128, scale=0.088, off=14, window=0,
+            mask=None, o=O, stream=None, flags=0)
+
+
+def call(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return pfa.prefill_attn_gqa_raw(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["L"], a["S"],
+                                    a["D"], a["scale"], a["off"], a["window"], a["mask"], a["o"],
+                                    a["stream"], a["flags"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1),
+    (dict(B=0), 2), (dict(Hq=0), 2), (dict(Hkv=-1), 2), (dict(L=0), 2), (dict(S=0), 2), (dict(D=0), 2),
+    (dict(B=2 ** 31 - 1, Hq=2 ** 31 - 1, L=2 ** 31 - 1, Hkv=1), 2),
+    (dict(Hq=6, Hkv=4), 3), (dict(Hq=7, Hkv=2), 3),
+    (dict(D=96), 4), (dict(D=256), 4), (dict(D=32), 4),
+    (dict(off=-1, window=5), 5),
+    (dict(scale=float("nan")), 6), (dict(scale=float("inf")), 6), (dict(scale=0.0), 6), (dict(scale=-0.1), 6),
+    (dict(q=Q + 8), 7), (dict(k=K + 2), 7), (dict(v=V + 4), 7), (dict(o=O + 1), 7),
+    (dict(o=Q), 8), (dict(o=Q + 16), 8), (dict(o=K + 4096), 8), (dict(o=V - 16), 8), (dict(mask=O + 3), 8),
+    (dict(flags=2), 9), (dict(flags=0x80000000), 9),
+], ids=lambda x: str(x))
+def test_invalid_arguments_rejected(lib, kw, code):
+    assert call(**kw) == code
+
+
+def test_validation_order(lib):
+    # null beats size beats gqa beats head dim beats mask args beats scale beats align beats alias
+    assert call(q=0, B=0) == 1
+    assert call(B=0, Hq=7) == 2
+    assert call(Hq=7, D=96) == 3
+    assert call(D=96, off=-1, window=3) == 4
+    assert call(off=-1, window=3, scale=0.0) == 5
+    assert call(scale=0.0, q=Q + 2) == 6
+    assert call(q=Q + 2, o=K) == 7
+    assert call(o=K, flags=4) == 8
+
+
+def test_o_adjacent_to_inputs_is_not_alias(lib):
+    # O may sit right after Q (half-open ranges); only a launch would follow, so check the rule on
+    # the mask instead, whose range is B*S bytes: a mask ending exactly at O is fine up to the
+    # launch, which needs a GPU, so assert only that the alias code is not returned.
+    q_bytes = 1 * 4 * 33 * 128 * 2
+    rc = call(q=O - q_bytes, k=K, v=V, o=O, flags=2)   # flags error proves alias check passed
+    assert rc == 9
+
+
+def test_binding_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 4, 8, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        pfa.prefill_attn_gqa(q, k, k)
+    with pytest.raises(ValueError, match="bfloat16"):
+        pfa.prefill_attn_gqa(q.float(), k, k)
+    with pytest.raises(TypeError):
+        pfa.prefill_attn_gqa([1], k, k)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(_binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _binding.library()
