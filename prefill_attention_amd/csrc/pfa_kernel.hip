@@ -38,6 +38,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
@@ -384,12 +385,9 @@ __global__ __launch_bounds__(NW * 64) void pfa_prefill_kernel(Params p) {
               (lds_i16x4*)(base + key_row * G::vStride + col));
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_i16x4*)(base + (key_row + 8) * G::vStride + col));
-          bf16x8 a;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            a[t] = __builtin_bit_cast(__bf16, lo[t]);
-            a[4 + t] = __builtin_bit_cast(__bf16, hi[t]);
-          }
+          // Join the two reads as one integer vector and reinterpret it whole: assembling the
+          // bf16 operand element by element from 16-bit integers is mis-lowered by the compiler.
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
         }
       }
