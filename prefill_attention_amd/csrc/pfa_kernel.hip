@@ -463,7 +463,7 @@ int launch_variant(const pfa::Launch& L) {
   return e == hipSuccess ? PFA_OK : PFA_ERR_LAUNCH;
 }
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 
 }  // namespace
 
