@@ -51,7 +51,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <int D>
 struct Geo {
   static constexpr int kStride = D + 8;   // K row pitch in LDS (bf16): 16-byte pad
-  static constexpr int vStride = D + 16;  // V row pitch: 32-byte pad for the transpose reads
+  // V row pitch: 320 B (D=128) / 192 B (D=64). The four rows of one 16-lane transpose read then
+  // start 64 B apart modulo 256 B, so the eight 32-byte pieces a half-wave reads hit distinct banks.
+  static constexpr int vStride = D + 32;
   static constexpr int kTile = kBN * kStride;
   static constexpr int vTile = kBN * vStride;
   static constexpr int kChunksPerRow = D / 8;  // 16-byte chunks
