@@ -9,8 +9,8 @@
 // visiting every tile.
 //
 // gfx950 design:
-//  * One workgroup = NW waves; each wave owns 32 query rows of one query head; the workgroup
-//    covers 32*NW consecutive rows.
+//  * One workgroup = 8 waves; each wave owns 32 query rows of one query head; the workgroup
+//    covers 256 consecutive rows. Waves w and w+4 share a SIMD.
 //  * Scores are computed transposed, S^T = K . Q^T, with v_mfma_f32_32x32x16_bf16. In the MFMA
 //    result lane l holds key rows 8j+4h+i (h = l/32) of query column l%32, so every lane owns one
 //    query row: row max and row sum are in-lane plus one exchange between the two lane halves.
@@ -18,8 +18,16 @@
 //    (exponentiated, rounded to BF16) are directly the B operand of that MFMA: the key order they
 //    imply is matched by reading V^T from LDS with ds_read_b64_tr_b16, which hands each lane four
 //    consecutive keys of one column. P never goes through LDS and V is never transposed by VALU.
-//  * K and V tiles (64 keys x D) are loaded with coalesced 16-byte global loads into registers one
-//    tile ahead, then written to a double-buffered LDS tile; one barrier per tile.
+//  * Software pipeline and ping-pong: a wave's work on tile t is GEMM1(t) (scores), SOFTMAX(t)
+//    and GEMM2(t) (P.V). A wave runs "GEMM1(t) + GEMM2(t-1)" as one MFMA phase and SOFTMAX(t) as
+//    one VALU phase. Waves 0-3 and 4-7 run these phases in opposite halves of each iteration
+//    (two barriers per iteration), so on every SIMD one wave feeds the matrix core while the
+//    other runs the exponentials. In the MFMA phase each LDS operand is read three MFMAs ahead.
+//  * K/V tiles (64 keys x D) go from HBM straight into LDS with global_load_lds_dwordx4 (each
+//    instruction writes 1 KB of consecutive LDS), into one of three stages: tile t+1 lands while
+//    tile t's K and tile t-1's V are read. Rows are unpadded; 16-byte chunks are XOR-swizzled
+//    per row so both the K reads (ds_read_b128, one row per lane) and the V transpose reads
+//    (four rows per 16 lanes) are free of bank conflicts.
 //  * Scores are scaled by scale*log2(e) inside the exp2 argument (one FMA per score).
 //  * The tile range of a workgroup is bounded by the causal and window edges; with a key mask a
 //    per-tile "any valid" bitmap (64 tiles per ballot) lets the loop jump over empty tiles; waves
@@ -38,26 +46,39 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kBN = 64;      // keys per tile
+constexpr int kBN = 64;  // keys per tile
 constexpr int kWaveRows = 32;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBM = kWaves * kWaveRows;  // query rows per workgroup
+constexpr int kStages = 3;
 constexpr int kXcds = 8;
+constexpr int kRing = 4;  // LDS operands in flight in the MFMA phase
 constexpr float kLog2e = 1.4426950408889634f;
+
+// sched_group_barrier masks
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 template <int D>
 struct Geo {
-  static constexpr int kStride = D + 8;   // K row pitch in LDS (bf16): 16-byte pad
-  // V row pitch: 320 B (D=128) / 192 B (D=64). The four rows of one 16-lane transpose read then
-  // start 64 B apart modulo 256 B, so the eight 32-byte pieces a half-wave reads hit distinct banks.
-  static constexpr int vStride = D + 32;
-  static constexpr int kTile = kBN * kStride;
-  static constexpr int vTile = kBN * vStride;
-  static constexpr int kChunksPerRow = D / 8;  // 16-byte chunks
-  static constexpr int kChunks = kBN * kChunksPerRow;
+  static constexpr int kRowBytes = 2 * D;              // unpadded K / V row in LDS
+  static constexpr int kTileBytes = kBN * kRowBytes;   // one K or V tile
+  static constexpr int kStageBytes = 2 * kTileBytes;   // K then V
+  static constexpr int kChunksPerRow = D / 8;          // 16-byte chunks per row
+  static constexpr int kRowsPerDma = 1024 / kRowBytes;  // rows written by one DMA instruction
+  static constexpr int kDmaPerTile = kTileBytes / 1024;
+  static constexpr int kDmaPerWave = kDmaPerTile / 4;  // per matrix, for each of waves 0-3
+  static constexpr int KQ = D / 16;  // MFMA k-steps over the head dimension
+  static constexpr int DB = D / 32;  // 32-wide output blocks
+  // Physical chunk of logical chunk c in row r is c ^ swz(r).
+  __device__ static int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 struct Params {
@@ -75,8 +96,14 @@ struct Params {
   int xcd_remap;
 };
 
-__device__ __forceinline__ float wave_max_halves(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+// max(x, x of lane l^32) with one v_permlane32_swap_b32 (a VALU lane exchange, no memory
+// access): swapping lanes 32-63 of one copy with lanes 0-31 of another leaves [lo, lo] and
+// [hi, hi]. It is written as inline asm because the compiler builtin, given two equal inputs,
+// returns its first result for both; the s_nop pads cover the VALU-write -> permlane hazard.
+__device__ __forceinline__ float max_with_partner_half(float x) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
 __device__ __forceinline__ bool any_zero_byte(uint32_t x) {
@@ -119,63 +146,57 @@ __device__ void key_mask_chunk(const uint8_t* mrow, int S, int t0, int lane, uin
   *all = __ballot(al);
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void pfa_prefill_kernel(Params p) {
+template <int D, bool KMASK>
+__global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   using G = Geo<D>;
-  constexpr int NT = NW * 64;
-  constexpr int BM = NW * kWaveRows;
-  constexpr int CPT = G::kChunks / NT;  // 16-byte chunks per thread per tile, for K and for V
-  static_assert(G::kChunks % NT == 0, "tile chunks must divide evenly");
-  constexpr int KQ = D / 16;  // MFMA k-steps over the head dimension
-  constexpr int DB = D / 32;  // 32-wide output blocks
+  constexpr int KQ = G::KQ;
+  constexpr int DB = G::DB;
+  constexpr int NG1 = 2 * KQ;  // GEMM1 MFMAs per tile
+  constexpr int NG2 = 4 * DB;  // GEMM2 MFMAs per tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][G::kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][G::vTile];
-  __shared__ __attribute__((aligned(16))) uint8_t m_lds[2][kBN];
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kStages * G::kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t m_lds[kStages][kBN];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
+  const bool group_a = wave < 4;  // waves w and w+4 share a SIMD and take opposite phases
 
   // ---- workgroup -> (b, kv head, query block, head in group) ----
-  long long item = blockIdx.x;
-  if (p.xcd_remap) {
-    const int per = p.n_wg / kXcds;
-    item = (long long)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-  }
-  const int g = (int)(item % p.group);
+  int item = blockIdx.x;
+  if (p.xcd_remap) item = (blockIdx.x % kXcds) * (p.n_wg / kXcds) + blockIdx.x / kXcds;
+  const int g = item % p.group;
   item /= p.group;
-  const int qrank = (int)(item % p.n_qblk);
+  const int qrank = item % p.n_qblk;
   item /= p.n_qblk;
-  const int hk = (int)(item % p.hkv);
-  const int b = (int)(item / p.hkv);
+  const int hk = item % p.hkv;
+  const int b = item / p.hkv;
   const bool causal = p.causal_offset >= 0;
   const int qblk = causal ? (p.n_qblk - 1 - qrank) : qrank;
   const int h = hk * p.group + g;
   const int L = p.lq, S = p.sk;
-  const long long off = p.causal_offset;
   const int W = p.window;
-  const int q0 = qblk * BM;
-  const int q1 = (q0 + BM) < L ? (q0 + BM) : L;
+  const int q0 = qblk * kBM;
+  const int q1 = (q0 + kBM) < L ? (q0 + kBM) : L;
 
   const uint16_t* kg = p.k + ((long long)b * p.hkv + hk) * (long long)S * D;
   const uint16_t* vg = p.v + ((long long)b * p.hkv + hk) * (long long)S * D;
-  const uint8_t* mrow = p.key_mask ? p.key_mask + (long long)b * S : nullptr;
-  const bool kmask = mrow != nullptr;
+  const uint8_t* mrow = KMASK ? p.key_mask + (long long)b * S : nullptr;
+  constexpr bool kmask = KMASK;
 
   // ---- key-tile range of the workgroup ----
   const int n_tiles = (S + kBN - 1) / kBN;
   int kt_lo = 0, kt_hi = n_tiles;
   if (!p.no_skip && causal) {
-    long long hi_key = (long long)q1 + off;  // exclusive
+    long long hi_key = (long long)q1 + p.causal_offset;  // exclusive
     if (hi_key > S) hi_key = S;
     kt_hi = (int)((hi_key + kBN - 1) / kBN);
     if (W > 0) {
-      long long lo_key = (long long)q0 + off - W + 1;
+      long long lo_key = (long long)q0 + p.causal_offset - W + 1;
       if (lo_key < 0) lo_key = 0;
-      long long t = lo_key / kBN;
+      const long long t = lo_key / kBN;
       kt_lo = (int)(t < n_tiles ? t : n_tiles);
     }
   }
@@ -213,208 +234,329 @@ __global__ __launch_bounds__(NW * 64) void pfa_prefill_kernel(Params p) {
   // ---- key-mask bitmap (per wave, 64 tiles per chunk) ----
   int mchunk = -1;
   uint64_t m_any = 0, m_all = 0;
-  auto ensure_chunk = [&](int kt) {
+  auto ensure_chunk = [&](int kt) __attribute__((always_inline)) {
     const int ch = kt >> 6;
     if (ch != mchunk) {
       key_mask_chunk(mrow, S, ch << 6, lane, &m_any, &m_all);
       mchunk = ch;
     }
   };
-  // Next tile >= k (and < kt_hi) to visit, or kt_hi. With a key mask and skipping on, tiles
-  // without a valid key are passed over; *all_valid tells whether every key of the returned tile
-  // is valid (no elementwise key masking needed).
-  auto next_tile = [&](int k, bool* all_valid) -> int {
-    *all_valid = true;
-    if (!kmask) return k < kt_hi ? k : kt_hi;
+  // Next tile >= k (and < kt_hi) to visit, or kt_hi, packed as (tile << 1) | all_valid. With a
+  // key mask and skipping on, tiles without a valid key are passed over; all_valid tells whether
+  // every key of the returned tile is valid (no elementwise key masking needed).
+  auto next_tile = [&](int k) __attribute__((always_inline)) -> int {
+    if (k >= kt_hi) return (kt_hi << 1) | 1;
+    if (!kmask) return (k << 1) | 1;
     while (k < kt_hi) {
       ensure_chunk(k);
-      if (p.no_skip) {
-        *all_valid = (m_all >> (k & 63)) & 1ull;
-        return k;
-      }
+      if (p.no_skip) return (k << 1) | (int)((m_all >> (k & 63)) & 1ull);
       const uint64_t bits = m_any >> (k & 63);
       if (bits) {
         const int t = k + __builtin_ctzll(bits);
-        if (t >= kt_hi) return kt_hi;
-        *all_valid = (m_all >> (t & 63)) & 1ull;
-        return t;
+        if (t >= kt_hi) return (kt_hi << 1) | 1;
+        return (t << 1) | (int)((m_all >> (t & 63)) & 1ull);
       }
       k = (k | 63) + 1;
     }
-    return kt_hi;
+    return (kt_hi << 1) | 1;
   };
 
-  // ---- tile staging ----
-  uint4 kreg[CPT], vreg[CPT];
+  // ---- tile staging: HBM -> LDS stage by DMA; the key-mask bytes through registers ----
+  // DMA instruction i of a matrix writes LDS bytes [1024 i, 1024 (i+1)) of the tile: lane l lands
+  // at row i*RPI + l/CPR, physical chunk l%CPR, and fetches the logical chunk that belongs there.
+  int dma_off_k[G::kDmaPerWave], dma_off_v[G::kDmaPerWave];  // element offsets within the tile
+  int dma_row[G::kDmaPerWave];
+  const int dma_wave = wave & 3;  // waves 0-3 fetch; the table is computed by all
+#pragma unroll
+  for (int j = 0; j < G::kDmaPerWave; ++j) {
+    const int i = dma_wave * G::kDmaPerWave + j;
+    const int row = i * G::kRowsPerDma + lane / G::kChunksPerRow;
+    const int pch = lane % G::kChunksPerRow;
+    dma_row[j] = row;
+    dma_off_k[j] = row * D + ((pch ^ G::swz_k(row)) * 8);
+    dma_off_v[j] = row * D + ((pch ^ G::swz_v(row)) * 8);
+  }
   uint8_t mreg = 0;
-  auto load_tile = [&](int kt) {
+  // One DMA instruction of a tile: part 2j is K block j of this wave, part 2j+1 is V block j.
+  // Only waves 0-3 fetch: they issue the next tile right after the last LDS operand read of their
+  // MFMA phase, where they would otherwise wait at the barrier for the softmax of waves 4-7.
+  constexpr int kDmaParts = 2 * G::kDmaPerWave;
+  auto issue_part = [&](int kt, int st, int part) __attribute__((always_inline)) {
+    const int j = part >> 1;
+    const bool is_v = part & 1;
     const long long key0 = (long long)kt * kBN;
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int ch = tid + r * NT;
-      const int row = ch / G::kChunksPerRow;
-      const int col = (ch % G::kChunksPerRow) * 8;
-      const long long key = key0 + row;
-      if (key < S) {
-        const long long o = key * D + col;
-        kreg[r] = *reinterpret_cast<const uint4*>(kg + o);
-        vreg[r] = *reinterpret_cast<const uint4*>(vg + o);
-      } else {
-        kreg[r] = make_uint4(0, 0, 0, 0);
-        vreg[r] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    if (kmask && tid < kBN) mreg = (key0 + tid < S) ? mrow[key0 + tid] : (uint8_t)0;
+    const int last_row = (int)((long long)S - 1 - key0);
+    int off = is_v ? dma_off_v[j] : dma_off_k[j];
+    if (dma_row[j] > last_row) off -= (dma_row[j] - last_row) * D;  // keys past S: re-read row S-1
+    const uint16_t* src = (is_v ? vg : kg) + key0 * D + off;
+    lds_char* dst = (lds_char*)lds_raw + st * G::kStageBytes + (is_v ? G::kTileBytes : 0) +
+                    (dma_wave * G::kDmaPerWave + j) * 1024;
+    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst,
+                                     16, 0, 0);
+    if (kmask && part == 0 && tid < kBN) mreg = (key0 + tid < S) ? mrow[key0 + tid] : (uint8_t)0;
   };
-  auto store_tile = [&](int buf) {
+  auto issue_tile = [&](int kt, int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int ch = tid + r * NT;
-      const int row = ch / G::kChunksPerRow;
-      const int col = (ch % G::kChunksPerRow) * 8;
-      *reinterpret_cast<uint4*>(&k_lds[buf][row * G::kStride + col]) = kreg[r];
-      *reinterpret_cast<uint4*>(&v_lds[buf][row * G::vStride + col]) = vreg[r];
-    }
-    if (kmask && tid < kBN) m_lds[buf][tid] = mreg;
+    for (int part = 0; part < kDmaParts; ++part) issue_part(kt, st, part);
+  };
+  auto finish_tile = [&](int st) __attribute__((always_inline)) {
+    if (kmask && tid < kBN) m_lds[st][tid] = mreg;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
   };
 
-  // ---- one tile of arithmetic for this wave ----
-  auto compute_tile = [&](int kt, int buf, bool tile_all_valid) {
+  // ---- per-lane LDS read addresses (byte offsets inside a stage) ----
+  // K (GEMM1 A operand): row l32 (+32 kb), logical chunk 2kk+hh -> address a_k ^ (32 kk).
+  int a_k;
+  {
+    const int x = G::swz_k(l32);
+    a_k = l32 * G::kRowBytes + 16 * (hh ^ (x & 1)) + 32 * (x >> 1);
+  }
+  // V^T (GEMM2 A operand, transpose reads): 16-lane group g16 reads rows 4(g16>>1)+r4 of a
+  // 16-key step, columns 32db + 16(g16&1) + 4cc -> address a_v ^ (64 db).
+  int a_v;
+  {
+    const int g16 = lane >> 4, loc = lane & 15, r4 = loc >> 2, cc = loc & 3;
+    const int row = 4 * (g16 >> 1) + r4;
+    const int sv = G::swz_v(row) >> 2;  // swizzle of the 64-byte column block
+    a_v = G::kTileBytes + row * G::kRowBytes + 64 * sv + 32 * (g16 & 1) + 8 * cc;
+  }
+
+  // ---- per-wave view of one tile: mask thresholds, skip and mask decisions ----
+  struct TileView {
+    int lim_tail, dc, dw;
+    bool live;       // some real row of this wave sees some key of the tile
+    bool need_mask;  // the tile straddles an edge for this wave
+  };
+  auto view_of = [&](int kt, bool tile_all_valid) __attribute__((always_inline)) -> TileView {
+    TileView tv;
     const long long key0 = (long long)kt * kBN;
-    // relative mask thresholds: row i = qw0 + ii, key j = key0 + jj
-    long long lim_tail_l = (long long)S - key0;
-    const int lim_tail = lim_tail_l < kBN ? (int)lim_tail_l : kBN;
-    int dc = 1 << 20, dw = -(1 << 20);
+    const long long lim_tail_l = (long long)S - key0;
+    tv.lim_tail = lim_tail_l < kBN ? (int)lim_tail_l : kBN;
+    tv.dc = 1 << 20;
+    tv.dw = -(1 << 20);
     if (causal) {
-      long long t = off + qw0 - key0;  // visible iff jj - ii <= dc
-      dc = t > 256 ? 256 : (t < -256 ? -256 : (int)t);
+      const long long t = (long long)p.causal_offset + qw0 - key0;  // visible iff jj-ii <= dc
+      tv.dc = t > 256 ? 256 : (t < -256 ? -256 : (int)t);
       if (W > 0) {
-        long long u = off - W + 1 + qw0 - key0;  // visible iff jj - ii >= dw
-        dw = u > 256 ? 256 : (u < -256 ? -256 : (int)u);
+        const long long u = (long long)p.causal_offset - W + 1 + qw0 - key0;  // jj-ii >= dw
+        tv.dw = u > 256 ? 256 : (u < -256 ? -256 : (int)u);
       }
     }
-    // Does the tile hold any visible cell for this wave's real rows?
-    if (!p.no_skip) {
-      int lo = dw > -ii_last ? dw : -ii_last;
-      int hi = dc < lim_tail - 1 ? dc : lim_tail - 1;
-      if (lo > hi) return;
-    }
-    const bool need_mask = lim_tail < kBN || (causal && (kBN - 1) > dc) ||
-                           (causal && W > 0 && -31 < dw) || !tile_all_valid;
+    const int lo = tv.dw > -ii_last ? tv.dw : -ii_last;
+    const int hi = tv.dc < tv.lim_tail - 1 ? tv.dc : tv.lim_tail - 1;
+    tv.live = wave_active && (p.no_skip || lo <= hi);
+    tv.need_mask = tv.lim_tail < kBN || (causal && (kBN - 1) > tv.dc) ||
+                   (causal && W > 0 && -31 < tv.dw) || !tile_all_valid;
+    return tv;
+  };
 
-    // S^T for two 32-key blocks
-    f32x16 s[2];
+  // ---- the MFMA phase: GEMM1 of one tile and/or GEMM2 of the previous one ----
+  f32x16 s[2];   // scores of a tile between GEMM1 and SOFTMAX
+  bf16x8 pb[4];  // probabilities of a tile between SOFTMAX and GEMM2
+
+  // GEMM1 of the current tile and GEMM2 of the previous one, steps alternating. Both always run:
+  // a wave with no scores to make runs GEMM1 for nothing, and a wave with no probabilities runs
+  // GEMM2 on pb = 0, which adds exact zeros to the accumulator (it starts at +0 and sums
+  // non-negative weights, so it is never -0 and acc + 0 == acc bit for bit).
+  auto mfma_phase = [&](int st1, int st2) __attribute__((always_inline)) {
+    const lds_char* base1 = (const lds_char*)lds_raw + st1 * G::kStageBytes;
+    const lds_char* base2 = (const lds_char*)lds_raw + st2 * G::kStageBytes;
+    auto load_g1 = [&](int j) __attribute__((always_inline)) -> bf16x8 {
+      const int kb = j / KQ, kk = j % KQ;
+      return *(const lds_bf16x8*)(base1 + kb * 32 * G::kRowBytes + (a_k ^ (32 * kk)));
+    };
+    auto load_g2 = [&](int j) __attribute__((always_inline)) -> bf16x8 {
+      const int kb = j / (2 * DB), c2 = (j / DB) & 1, db = j % DB;
+      const lds_char* pr = base2 + (kb * 32 + 16 * c2) * G::kRowBytes + (a_v ^ (64 * db));
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pr);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pr + 8 * G::kRowBytes));
+      // Join the two reads as one integer vector and reinterpret it whole: assembling the bf16
+      // operand element by element from 16-bit integers is mis-lowered by the compiler.
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto mma_g1 = [&](int j, const bf16x8& a) __attribute__((always_inline)) {
+      const int kb = j / KQ, kk = j % KQ;
+      if (kk == 0) {
+        f32x16 z;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] = 0.0f;
-      const uint16_t* kb_ptr = &k_lds[buf][(kb * 32 + l32) * G::kStride + 8 * hh];
-#pragma unroll
-      for (int kk = 0; kk < KQ; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ptr + 16 * kk);
+        for (int v = 0; v < 16; ++v) z[v] = 0.0f;
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], z, 0, 0, 0);
+      } else {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s[kb], 0, 0, 0);
       }
+    };
+    auto mma_g2 = [&](int j, const bf16x8& a) __attribute__((always_inline)) {
+      const int kb = j / (2 * DB), c2 = (j / DB) & 1, db = j % DB;
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[2 * kb + c2], acc[db], 0, 0, 0);
+    };
+    bf16x8 ring[kRing];
+    constexpr int NS = NG1 + NG2;  // alternate: even steps GEMM1, odd steps GEMM2
+#pragma unroll
+    for (int m = 0; m < NS + kRing - 1; ++m) {
+      if (m < NS) {
+        if (m & 1) {
+          ring[m % kRing] = load_g2(m >> 1);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        } else {
+          ring[m % kRing] = load_g1(m >> 1);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+      }
+      const int u = m - (kRing - 1);
+      if (u >= 0) {
+        if (u & 1) mma_g2(u >> 1, ring[u % kRing]);
+        else mma_g1(u >> 1, ring[u % kRing]);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      }
     }
+  };
 
-    if (need_mask) {
+  // ---- the VALU phase: mask, online softmax, P in bf16, accumulator rescale ----
+  auto softmax = [&](const TileView& tv, int st) __attribute__((always_inline)) {
+    if (tv.need_mask) {
+      // Row ii = l32 sees tile keys jj in [lo, lo + span] (causal, window and tail bounds),
+      // tested as one unsigned compare per score; span < 0 means the row sees nothing.
       const int ii = l32;
+      int lo = ii + tv.dw;
+      if (lo < 0) lo = 0;
+      int hi = ii + tv.dc;
+      if (hi > tv.lim_tail - 1) hi = tv.lim_tail - 1;
+      unsigned span = (unsigned)(hi - lo);
+      if (hi < lo) {
+        lo = kBN;  // every jj - lo is then negative, i.e. a huge unsigned value
+        span = 0;
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          uint32_t mb = 0xFFFFFFFFu;
-          if (kmask)
-            mb = *reinterpret_cast<const uint32_t*>(&m_lds[buf][kb * 32 + 8 * j + 4 * hh]);
+          const uint32_t mb =
+              kmask ? *reinterpret_cast<const uint32_t*>(&m_lds[st][kb * 32 + 8 * j + 4 * hh])
+                    : 0xFFFFFFFFu;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int jj = kb * 32 + 8 * j + 4 * hh + i;
-            const int rel = jj - ii;
-            bool vis = jj < lim_tail && rel <= dc && rel >= dw && ((mb >> (8 * i)) & 0xFFu) != 0u;
-            if (!vis) s[kb][4 * j + i] = -INFINITY;
+            const bool vis = ((unsigned)(jj - lo) <= span) & (((mb >> (8 * i)) & 0xFFu) != 0u);
+            s[kb][4 * j + i] = vis ? s[kb][4 * j + i] : -INFINITY;
           }
         }
       }
     }
-
-    // online softmax (per lane: one query row, 32 of the tile's 64 keys)
-    float mx = s[0][0];
+    // per lane: one query row, 32 of the tile's 64 keys. Short dependency chains: a tree of
+    // 3-input maxima, the cross-half exchange as a VALU lane swap, independent exponentials and
+    // four partial sums.
+    float r[32];
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
+    for (int v = 0; v < 16; ++v) {
+      r[v] = s[0][v];
+      r[16 + v] = s[1][v];
+    }
+    float t1[11];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[1][v]);
-    mx = wave_max_halves(mx);
+    for (int i = 0; i < 10; ++i) t1[i] = fmaxf(fmaxf(r[3 * i], r[3 * i + 1]), r[3 * i + 2]);
+    t1[10] = fmaxf(r[30], r[31]);
+    const float t2a = fmaxf(fmaxf(t1[0], t1[1]), t1[2]);
+    const float t2b = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
+    const float t2c = fmaxf(fmaxf(t1[6], t1[7]), t1[8]);
+    const float t2d = fmaxf(t1[9], t1[10]);
+    float mx = fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d));
+    mx = max_with_partner_half(mx);
     const float m_new = fmaxf(m_run, mx);
     const float ms_new = (m_new == -INFINITY) ? 0.0f : m_new * c;
     const float ms_old = (m_run == -INFINITY) ? -INFINITY : m_run * c;
     const float alpha = __builtin_amdgcn_exp2f(ms_old - ms_new);
     m_run = m_new;
-
-    float lsum = 0.0f;
+    float e[32];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int v = 0; v < 32; ++v) e[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(r[v], c, -ms_new));
+    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][v], c, -ms_new));
-        s[kb][v] = e;
-        lsum += e;
-      }
+    for (int v = 0; v < 32; ++v) ps[v & 3] += e[v];
+    const float lsum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) pb[q4][t] = (__bf16)e[8 * q4 + t];
     l_run = alpha * l_run + lsum;
+    // the accumulator gets this tile's P.V next; rescale it first unless no row's max moved
     if (!__all(alpha == 1.0f)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
     }
-
-    // O^T += V^T . P^T
-    const int g16 = lane >> 4;
-    const int loc = lane & 15;
-    const int r4 = loc >> 2;
-    const int cc = loc & 3;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        bf16x8 pb;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) pb[t] = (__bf16)s[kb][8 * c2 + t];
-        const int key_row = kb * 32 + 16 * c2 + 4 * (g16 >> 1) + r4;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int col = 32 * db + 16 * (g16 & 1) + 4 * cc;
-          lds_u16* base = (lds_u16*)(&v_lds[buf][0]);
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(base + key_row * G::vStride + col));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(base + (key_row + 8) * G::vStride + col));
-          // Join the two reads as one integer vector and reinterpret it whole: assembling the
-          // bf16 operand element by element from 16-bit integers is mis-lowered by the compiler.
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
-        }
-      }
-    }
   };
 
-  // ---- main loop over key tiles ----
-  bool all_cur = true;
-  int kt = next_tile(kt_lo, &all_cur);
-  if (kt < kt_hi) {
-    load_tile(kt);
-    store_tile(0);
+  // ---- main loop ----
+  // An iteration works on tile `cur` (its K in stage st_cur), tile `prv` (its V in stage st_prv)
+  // and fetches tile `nxt` into the third stage. Each half of an iteration ends with a barrier;
+  // a wave runs its MFMA phase in one half and its softmax phase in the other (group A: MFMA
+  // first). Group A issues the fetch of `nxt` right after its MFMA phase; it lands during the
+  // second half and is waited for before the closing barrier.
+  {
+    // zero every stage once, so that a stage never read by a real tile holds finite data
+    uint4* z = reinterpret_cast<uint4*>(lds_raw);
+    for (int i = tid; i < kStages * G::kStageBytes / 16; i += kThreads) z[i] = make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) pb[i][t] = (__bf16)0.0f;
+  __syncthreads();
+  int packed = next_tile(kt_lo);
+  int cur = packed >> 1;
+  bool all_cur = packed & 1;
+  if (cur < kt_hi) {
+    if (group_a) issue_tile(cur, 0);
+    finish_tile(0);
   }
   __syncthreads();
-  int buf = 0;
-  while (kt < kt_hi) {
-    bool all_nxt = true;
-    const int nk = next_tile(kt + 1, &all_nxt);
-    if (nk < kt_hi) load_tile(nk);
-    if (wave_active) compute_tile(kt, buf, all_cur);
-    if (nk < kt_hi) store_tile(buf ^ 1);
+  int prv = kt_hi;
+  TileView tv_cur{}, tv_prv{};
+  tv_prv.live = false;
+  int st_cur = 0, st_prv = kStages - 1;
+  auto softmax_phase = [&](const TileView& tv, int st) __attribute__((always_inline)) {
+    if (tv.live) {
+      softmax(tv, st);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) pb[i][t] = (__bf16)0.0f;
+    }
+  };
+  while (cur < kt_hi || prv < kt_hi) {
+    const int packed_nxt = next_tile(cur + 1 <= kt_hi ? cur + 1 : kt_hi);
+    const int nxt = packed_nxt >> 1;
+    const bool all_nxt = packed_nxt & 1;
+    const int st_nxt = st_cur + 1 == kStages ? 0 : st_cur + 1;
+    if (cur < kt_hi) {
+      tv_cur = view_of(cur, all_cur);
+    } else {
+      tv_cur.live = false;
+    }
+    // first half
+    if (group_a) {
+      mfma_phase(st_cur, st_prv);
+      if (nxt < kt_hi) issue_tile(nxt, st_nxt);
+    } else {
+      softmax_phase(tv_prv, st_prv);
+    }
+    // Phase alignment only: no LDS data is produced in the first half and consumed in the second
+    // (the fetch in flight targets the stage nobody reads this iteration), so a bare s_barrier is
+    // enough. A full __syncthreads would make waves 0-3 wait here for the fetch to land.
+    __builtin_amdgcn_s_barrier();
+    // second half
+    if (group_a) softmax_phase(tv_cur, st_cur);
+    else mfma_phase(st_cur, st_prv);
+    if (nxt < kt_hi) finish_tile(st_nxt);
     __syncthreads();
-    kt = nk;
+    prv = cur;
+    tv_prv = tv_cur;
+    st_prv = st_cur;
+    cur = nxt;
     all_cur = all_nxt;
-    buf ^= 1;
+    st_cur = st_nxt;
   }
 
   // ---- epilogue: O = acc / l, rows without visible keys -> 0 ----
@@ -436,9 +578,8 @@ __global__ __launch_bounds__(NW * 64) void pfa_prefill_kernel(Params p) {
   }
 }
 
-template <int D, int NW>
+template <int D>
 int launch_variant(const pfa::Launch& L) {
-  constexpr int BM = NW * kWaveRows;
   Params p;
   p.q = static_cast<const uint16_t*>(L.q);
   p.k = static_cast<const uint16_t*>(L.k);
@@ -454,24 +595,24 @@ int launch_variant(const pfa::Launch& L) {
   p.causal_offset = L.causal_offset;
   p.window = L.window;
   p.no_skip = (L.flags & PFA_FLAG_NO_SKIP) ? 1 : 0;
-  p.n_qblk = (L.lq + BM - 1) / BM;
+  p.n_qblk = (L.lq + kBM - 1) / kBM;
   const long long n = (long long)L.batch * L.hq * p.n_qblk;
   p.n_wg = (int)n;
   p.xcd_remap = (n % kXcds) == 0 ? 1 : 0;
   void* args[] = {&p};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pfa_prefill_kernel<D, NW>),
-                                 dim3((unsigned)n), dim3(NW * 64), args, 0,
+  const void* fn = L.key_mask ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, true>)
+                             : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, false>);
+  hipError_t e = hipLaunchKernel(fn,
+                                 dim3((unsigned)n), dim3(kThreads), args, 0,
                                  static_cast<hipStream_t>(L.stream));
   return e == hipSuccess ? PFA_OK : PFA_ERR_LAUNCH;
 }
-
-constexpr int kWaves = 8;
 
 }  // namespace
 
 namespace pfa {
 
-int rows_per_block(int) { return kWaves * kWaveRows; }
+int rows_per_block(int) { return kBM; }
 
 long long grid_blocks(const Launch& p) {
   const long long bm = rows_per_block(p.d);
@@ -479,8 +620,8 @@ long long grid_blocks(const Launch& p) {
 }
 
 int launch_prefill(const Launch& p) {
-  if (p.d == 128) return launch_variant<128, kWaves>(p);
-  return launch_variant<64, kWaves>(p);
+  if (p.d == 128) return launch_variant<128>(p);
+  return launch_variant<64>(p);
 }
 
 }  // namespace pfa
