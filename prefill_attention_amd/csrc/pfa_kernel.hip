@@ -60,6 +60,7 @@ constexpr int kStages = 3;
 constexpr int kXcds = 8;
 constexpr int kRing = 4;  // LDS operands in flight in the MFMA phase
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyLog2 = 8.0f;  // reference-max slack of the lazy rescale (P <= 2^8)
 
 // sched_group_barrier masks
 constexpr int kSchedMfma = 0x008;
@@ -227,8 +228,8 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[db][v] = 0.0f;
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
+  float m_run = -INFINITY;  // reference maximum the exponentials are taken against
+  float l_run = 0.0f;       // this lane's half of the row sum of P
   const float c = p.c;
 
   // ---- key-mask bitmap (per wave, 64 tiles per chunk) ----
@@ -461,30 +462,37 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     const float t2d = fmaxf(t1[9], t1[10]);
     float mx = fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d));
     mx = max_with_partner_half(mx);
-    const float m_new = fmaxf(m_run, mx);
+    // Lazy rescaling: the exponentials are taken against the reference maximum m_run, which is
+    // raised (and the accumulators rescaled) only when some row's tile maximum exceeds it by more
+    // than 2^8 in probability, or a row meets its first visible key. Otherwise P <= 256, exact
+    // arithmetic on both sides of the final a / l. A fully masked tile never raises the reference,
+    // so visiting it (no-skip mode) changes nothing.
+    const bool need = (m_run == -INFINITY) ? (mx != -INFINITY) : ((mx - m_run) * c > kLazyLog2);
+    const bool raise = __any(need);
+    const float m_new = raise ? fmaxf(m_run, mx) : m_run;
     const float ms_new = (m_new == -INFINITY) ? 0.0f : m_new * c;
-    const float ms_old = (m_run == -INFINITY) ? -INFINITY : m_run * c;
-    const float alpha = __builtin_amdgcn_exp2f(ms_old - ms_new);
-    m_run = m_new;
-    float e[32];
-#pragma unroll
-    for (int v = 0; v < 32; ++v) e[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(r[v], c, -ms_new));
     float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int v = 0; v < 32; ++v) ps[v & 3] += e[v];
-    const float lsum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) pb[q4][t] = (__bf16)e[8 * q4 + t];
-    l_run = alpha * l_run + lsum;
-    // the accumulator gets this tile's P.V next; rescale it first unless no row's max moved
-    if (!__all(alpha == 1.0f)) {
+      for (int t = 0; t < 8; ++t) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(r[8 * q4 + t], c, -ms_new));
+        ps[t & 3] += e;
+        pb[q4][t] = (__bf16)e;
+      }
+    const float lsum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    if (raise) {
+      // the accumulator gets this tile's P.V next; rescale it to the raised reference first
+      const float ms_old = (m_run == -INFINITY) ? -INFINITY : m_run * c;
+      const float alpha = __builtin_amdgcn_exp2f(ms_old - ms_new);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+      l_run *= alpha;
     }
+    m_run = m_new;
+    l_run += lsum;
   };
 
   // ---- main loop ----
