@@ -60,7 +60,9 @@ constexpr int kStages = 3;
 constexpr int kXcds = 8;
 constexpr int kRing = 4;  // LDS operands in flight in the MFMA phase
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazyLog2 = 8.0f;  // reference-max slack of the lazy rescale (P <= 2^8)
+constexpr float kLazyLog2 = 8.0f;
+// dword 3 of a raw buffer descriptor (32-bit data format, no swizzle, bounds checked per byte)
+constexpr int kBufferFlags = 0x00020000;  // reference-max slack of the lazy rescale (P <= 2^8)
 
 // sched_group_barrier masks
 constexpr int kSchedMfma = 0x008;
@@ -74,7 +76,7 @@ struct Geo {
   static constexpr int kChunksPerRow = D / 8;          // 16-byte chunks per row
   static constexpr int kRowsPerDma = 1024 / kRowBytes;  // rows written by one DMA instruction
   static constexpr int kDmaPerTile = kTileBytes / 1024;
-  static constexpr int kDmaPerWave = kDmaPerTile / 4;  // per matrix, for each of waves 0-3
+  static constexpr int kDmaPerWave = kDmaPerTile / 4;  // per wave of the group fetching a matrix
   static constexpr int KQ = D / 16;  // MFMA k-steps over the head dimension
   static constexpr int DB = D / 32;  // 32-wide output blocks
   // Physical chunk of logical chunk c in row r is c ^ swz(r).
@@ -96,6 +98,24 @@ struct Params {
   int n_wg;
   int xcd_remap;
 };
+
+// N DMA instructions of one wave from a buffer of `nrec` bytes at `base` (wave-uniform) into LDS:
+// instruction j writes lane l's 16 bytes, read from byte offset off[j] of the buffer, to LDS
+// address dst + 1024 j + 16 l. Reads at or past nrec return zeros.
+template <int N>
+__device__ __forceinline__ void dma_rows(const void* base, int nrec, lds_char* dst, const unsigned* off) {
+  __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nrec, kBufferFlags);
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16,
+                                             off[j], 0, 0, 0);
+}
+
+// Workgroup barrier that waits only for this wave's LDS instructions, not for its DMA still in
+// flight; the memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // max(x, x of lane l^32) with one v_permlane32_swap_b32 (a VALU lane exchange, no memory
 // access): swapping lanes 32-63 of one copy with lanes 0-31 of another leaves [lo, lo] and
@@ -263,46 +283,45 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   };
 
   // ---- tile staging: HBM -> LDS stage by DMA; the key-mask bytes through registers ----
-  // DMA instruction i of a matrix writes LDS bytes [1024 i, 1024 (i+1)) of the tile: lane l lands
-  // at row i*RPI + l/CPR, physical chunk l%CPR, and fetches the logical chunk that belongs there.
-  int dma_off_k[G::kDmaPerWave], dma_off_v[G::kDmaPerWave];  // element offsets within the tile
-  int dma_row[G::kDmaPerWave];
-  const int dma_wave = wave & 3;  // waves 0-3 fetch; the table is computed by all
+  // Waves 0-3 fetch K, waves 4-7 fetch V, each right after its own MFMA phase. A fetch is a
+  // buffer load with the LDS as destination: the buffer descriptor starts at the tile's first key
+  // and covers only keys < S, so rows past the end of the cache come back as zeros without any
+  // per-lane test. DMA instruction i of a matrix writes LDS bytes [1024 i, 1024 (i+1)) of the
+  // tile: lane l lands at row i*RPI + l/CPR, physical chunk l%CPR, and fetches the logical chunk
+  // that belongs there (byte offset dma_off[j] within the tile). The table is fixed per wave.
+  unsigned dma_off[G::kDmaPerWave];
+  const int w4 = wave & 3;
 #pragma unroll
   for (int j = 0; j < G::kDmaPerWave; ++j) {
-    const int i = dma_wave * G::kDmaPerWave + j;
+    const int i = w4 * G::kDmaPerWave + j;
     const int row = i * G::kRowsPerDma + lane / G::kChunksPerRow;
     const int pch = lane % G::kChunksPerRow;
-    dma_row[j] = row;
-    dma_off_k[j] = row * D + ((pch ^ G::swz_k(row)) * 8);
-    dma_off_v[j] = row * D + ((pch ^ G::swz_v(row)) * 8);
+    const int sw = group_a ? G::swz_k(row) : G::swz_v(row);
+    dma_off[j] = (unsigned)(row * G::kRowBytes + 16 * (pch ^ sw));
   }
+  // wave-uniform values, made scalar explicitly (the compiler cannot see that tid >> 6 is)
+  const uint16_t* dma_src = group_a ? kg : vg;
+  const int dma_lds = __builtin_amdgcn_readfirstlane((group_a ? 0 : G::kTileBytes) + w4 * G::kDmaPerWave * 1024);
   uint8_t mreg = 0;
-  // One DMA instruction of a tile: part 2j is K block j of this wave, part 2j+1 is V block j.
-  // Only waves 0-3 fetch: they issue the next tile right after the last LDS operand read of their
-  // MFMA phase, where they would otherwise wait at the barrier for the softmax of waves 4-7.
-  constexpr int kDmaParts = 2 * G::kDmaPerWave;
-  auto issue_part = [&](int kt, int st, int part) __attribute__((always_inline)) {
-    const int j = part >> 1;
-    const bool is_v = part & 1;
+  // this wave's share of matrix (K for waves 0-3, V for 4-7) of tile kt into stage st
+  auto issue = [&](int kt, int st) __attribute__((always_inline)) {
     const long long key0 = (long long)kt * kBN;
-    const int last_row = (int)((long long)S - 1 - key0);
-    int off = is_v ? dma_off_v[j] : dma_off_k[j];
-    if (dma_row[j] > last_row) off -= (dma_row[j] - last_row) * D;  // keys past S: re-read row S-1
-    const uint16_t* src = (is_v ? vg : kg) + key0 * D + off;
-    lds_char* dst = (lds_char*)lds_raw + st * G::kStageBytes + (is_v ? G::kTileBytes : 0) +
-                    (dma_wave * G::kDmaPerWave + j) * 1024;
-    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst,
-                                     16, 0, 0);
-    if (kmask && part == 0 && tid < kBN) mreg = (key0 + tid < S) ? mrow[key0 + tid] : (uint8_t)0;
+    const long long rows = (long long)S - key0;
+    const int nrec = (rows < kBN ? (int)rows : kBN) * G::kRowBytes;
+    const uintptr_t base = reinterpret_cast<uintptr_t>(dma_src + key0 * D);
+    // readfirstlane returns int: go through unsigned so the low word is not sign-extended
+    const unsigned base_hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(base >> 32));
+    const unsigned base_lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)base);
+    const uintptr_t base_u = ((uintptr_t)base_hi << 32) | (uintptr_t)base_lo;
+    lds_char* dst = (lds_char*)lds_raw + st * G::kStageBytes + dma_lds;
+    dma_rows<G::kDmaPerWave>(reinterpret_cast<const void*>(base_u), __builtin_amdgcn_readfirstlane(nrec),
+                             dst, dma_off);
+    if (kmask && tid < kBN) mreg = (key0 + tid < S) ? mrow[key0 + tid] : (uint8_t)0;
   };
-  auto issue_tile = [&](int kt, int st) __attribute__((always_inline)) {
-#pragma unroll
-    for (int part = 0; part < kDmaParts; ++part) issue_part(kt, st, part);
-  };
-  auto finish_tile = [&](int st) __attribute__((always_inline)) {
+  // wait for this wave's fetches; waves 0-3 also publish the tile's mask bytes
+  auto finish = [&](int st) __attribute__((always_inline)) {
     if (kmask && tid < kBN) m_lds[st][tid] = mreg;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   };
 
   // ---- per-lane LDS read addresses (byte offsets inside a stage) ----
@@ -515,8 +534,8 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   int cur = packed >> 1;
   bool all_cur = packed & 1;
   if (cur < kt_hi) {
-    if (group_a) issue_tile(cur, 0);
-    finish_tile(0);
+    issue(cur, 0);
+    finish(0);
   }
   __syncthreads();
   int prv = kt_hi;
@@ -546,19 +565,23 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     // first half
     if (group_a) {
       mfma_phase(st_cur, st_prv);
-      if (nxt < kt_hi) issue_tile(nxt, st_nxt);
+      if (nxt < kt_hi) issue(nxt, st_nxt);  // K of tile nxt
     } else {
       softmax_phase(tv_prv, st_prv);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // V of tile cur (fetched last iteration) has landed
     }
-    // Phase alignment only: no LDS data is produced in the first half and consumed in the second
-    // (the fetch in flight targets the stage nobody reads this iteration), so a bare s_barrier is
-    // enough. A full __syncthreads would make waves 0-3 wait here for the fetch to land.
+    // Nothing stored to LDS in the first half is read in the second (the K in flight targets the
+    // stage nobody reads this iteration), so the middle barrier only aligns the phases.
     __builtin_amdgcn_s_barrier();
     // second half
-    if (group_a) softmax_phase(tv_cur, st_cur);
-    else mfma_phase(st_cur, st_prv);
-    if (nxt < kt_hi) finish_tile(st_nxt);
-    __syncthreads();
+    if (group_a) {
+      softmax_phase(tv_cur, st_cur);
+      if (nxt < kt_hi) finish(st_nxt);
+    } else {
+      mfma_phase(st_cur, st_prv);
+      if (nxt < kt_hi) issue(nxt, st_nxt);  // V of tile nxt: first read one iteration later
+    }
+    lds_barrier();
     prv = cur;
     tv_prv = tv_cur;
     st_prv = st_cur;
