@@ -49,6 +49,9 @@ extern "C" {
 /* causal_offset < 0 selects bidirectional attention (no causal term). */
 #define PFA_NO_CAUSAL (-1)
 
+/* Largest L and S accepted: rows and keys are indexed with 32-bit integers in the kernel. */
+#define PFA_MAX_LEN 1073741824 /* 2^30 */
+
 /* Visit every key tile of the grid and mask elementwise instead of skipping fully masked tiles.
  * Exists for the bit-identity check: the result must equal the default (skipping) call bit for
  * bit. */
@@ -57,7 +60,7 @@ extern "C" {
 enum pfa_status {
   PFA_OK = 0,
   PFA_ERR_NULL = 1,      /* Q, K, V or O is NULL                                               */
-  PFA_ERR_SIZE = 2,      /* a size < 1, or a size product / launch grid does not fit            */
+  PFA_ERR_SIZE = 2,      /* a size < 1, L or S > PFA_MAX_LEN, or a size product / grid too big  */
   PFA_ERR_GQA = 3,       /* Hq is not a multiple of Hkv                                         */
   PFA_ERR_HEAD_DIM = 4,  /* D is not 64 or 128                                                  */
   PFA_ERR_MASK_ARGS = 5, /* window > 0 without the causal term                                  */

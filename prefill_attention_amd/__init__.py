@@ -6,6 +6,7 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     FLAG_NO_SKIP,
     LIB_PATH,
+    MAX_LEN,
     NO_CAUSAL,
     STATUS,
     PfaError,

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libpfa.so")
 # Mirrors of include/pfa.h
 NO_CAUSAL = -1
 FLAG_NO_SKIP = 1
+MAX_LEN = 1 << 30
 STATUS = {
     0: "PFA_OK", 1: "PFA_ERR_NULL", 2: "PFA_ERR_SIZE", 3: "PFA_ERR_GQA", 4: "PFA_ERR_HEAD_DIM",
     5: "PFA_ERR_MASK_ARGS", 6: "PFA_ERR_SCALE", 7: "PFA_ERR_ALIGN", 8: "PFA_ERR_ALIAS",

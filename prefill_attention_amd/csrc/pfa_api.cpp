@@ -27,6 +27,8 @@ int validate(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv
              void* O, unsigned flags) {
   if (!Q || !K || !V || !O) return PFA_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || S < 1 || D < 1) return PFA_ERR_SIZE;
+  // The kernel indexes rows and keys with 32-bit integers (with headroom for tile rounding).
+  if (L > PFA_MAX_LEN || S > PFA_MAX_LEN) return PFA_ERR_SIZE;
   // Element counts must fit comfortably in 64 bits; byte offsets are formed in 64 bits.
   const long long lim = LLONG_MAX / 4;
   long long q_elems, kv_elems, t;

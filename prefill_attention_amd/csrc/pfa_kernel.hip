@@ -47,6 +47,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -60,6 +62,7 @@ constexpr int kStages = 3;
 constexpr int kXcds = 8;
 constexpr int kRing = 4;  // LDS operands in flight in the MFMA phase
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr float kLazyLog2 = 8.0f;
 // dword 3 of a raw buffer descriptor (32-bit data format, no swizzle, bounds checked per byte)
 constexpr int kBufferFlags = 0x00020000;  // reference-max slack of the lazy rescale (P <= 2^8)
@@ -117,6 +120,12 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Maxima of scores with the IEEE 754-2019 maximum (NaN-propagating), which maps to
+// v_maximum3_f32 with no input quieting; fmaxf would first canonicalize every MFMA result.
+// Scores are never NaN here (finite inputs, -inf for masked keys).
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3(float a, float b, float c) { return max2(max2(a, b), c); }
+
 // max(x, x of lane l^32) with one v_permlane32_swap_b32 (a VALU lane exchange, no memory
 // access): swapping lanes 32-63 of one copy with lanes 0-31 of another leaves [lo, lo] and
 // [hi, hi]. It is written as inline asm because the compiler builtin, given two equal inputs,
@@ -124,7 +133,7 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ float max_with_partner_half(float x) {
   unsigned a = __builtin_bit_cast(unsigned, x), b = a;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  return max2(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
 __device__ __forceinline__ bool any_zero_byte(uint32_t x) {
@@ -248,8 +257,11 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[db][v] = 0.0f;
-  float m_run = -INFINITY;  // reference maximum the exponentials are taken against
-  float l_run = 0.0f;       // this lane's half of the row sum of P
+  // Running state of the lane's query row: mref is the reference maximum the exponentials are
+  // taken against, in the base-2 exponent domain (scores times c; -inf before the row has seen a
+  // key), l_run this lane's half of the row sum of P.
+  float mref = -INFINITY;
+  float l_run = 0.0f;
   const float c = p.c;
 
   // ---- key-mask bitmap (per wave, 64 tiles per chunk) ----
@@ -347,26 +359,30 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     bool live;       // some real row of this wave sees some key of the tile
     bool need_mask;  // the tile straddles an edge for this wave
   };
+  // Row ii of the wave sees tile key jj iff dw <= jj - ii <= dc and jj < lim_tail. The causal
+  // and window bounds relative to key 0 are precomputed per wave and saturated (keys and rows fit
+  // in 31 bits), so the per-tile view is a few branch-free integer operations; with no causal
+  // term dc is pinned at +256 and with no window dw at -256, i.e. no bound inside a tile.
+  const int cbase = [&] {
+    if (!causal) return S + 512;
+    const long long t = (long long)p.causal_offset + qw0;
+    return (int)(t < -512 ? -512 : (t > (long long)S + 512 ? (long long)S + 512 : t));
+  }();
+  const int wbase = [&] {
+    if (!causal || W <= 0) return -512;
+    const long long t = (long long)p.causal_offset - W + 1 + qw0;
+    return (int)(t < -512 ? -512 : (t > (long long)S + 512 ? (long long)S + 512 : t));
+  }();
   auto view_of = [&](int kt, bool tile_all_valid) __attribute__((always_inline)) -> TileView {
     TileView tv;
-    const long long key0 = (long long)kt * kBN;
-    const long long lim_tail_l = (long long)S - key0;
-    tv.lim_tail = lim_tail_l < kBN ? (int)lim_tail_l : kBN;
-    tv.dc = 1 << 20;
-    tv.dw = -(1 << 20);
-    if (causal) {
-      const long long t = (long long)p.causal_offset + qw0 - key0;  // visible iff jj-ii <= dc
-      tv.dc = t > 256 ? 256 : (t < -256 ? -256 : (int)t);
-      if (W > 0) {
-        const long long u = (long long)p.causal_offset - W + 1 + qw0 - key0;  // jj-ii >= dw
-        tv.dw = u > 256 ? 256 : (u < -256 ? -256 : (int)u);
-      }
-    }
-    const int lo = tv.dw > -ii_last ? tv.dw : -ii_last;
-    const int hi = tv.dc < tv.lim_tail - 1 ? tv.dc : tv.lim_tail - 1;
-    tv.live = wave_active && (p.no_skip || lo <= hi);
-    tv.need_mask = tv.lim_tail < kBN || (causal && (kBN - 1) > tv.dc) ||
-                   (causal && W > 0 && -31 < tv.dw) || !tile_all_valid;
+    const int key0 = kt * kBN;
+    tv.lim_tail = min(S - key0, kBN);
+    tv.dc = max(min(cbase - key0, 256), -256);
+    tv.dw = max(min(wbase - key0, 256), -256);
+    const int lo = max(tv.dw, -ii_last);
+    const int hi = min(tv.dc, tv.lim_tail - 1);
+    tv.live = wave_active & ((p.no_skip != 0) | (lo <= hi));
+    tv.need_mask = (tv.lim_tail < kBN) | (tv.dc < kBN - 1) | (tv.dw > -31) | !tile_all_valid;
     return tv;
   };
 
@@ -471,46 +487,54 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
       r[v] = s[0][v];
       r[16 + v] = s[1][v];
     }
-    float t1[11];
+    float t1[12];
 #pragma unroll
-    for (int i = 0; i < 10; ++i) t1[i] = fmaxf(fmaxf(r[3 * i], r[3 * i + 1]), r[3 * i + 2]);
-    t1[10] = fmaxf(r[30], r[31]);
-    const float t2a = fmaxf(fmaxf(t1[0], t1[1]), t1[2]);
-    const float t2b = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
-    const float t2c = fmaxf(fmaxf(t1[6], t1[7]), t1[8]);
-    const float t2d = fmaxf(t1[9], t1[10]);
-    float mx = fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d));
-    mx = max_with_partner_half(mx);
-    // Lazy rescaling: the exponentials are taken against the reference maximum m_run, which is
-    // raised (and the accumulators rescaled) only when some row's tile maximum exceeds it by more
-    // than 2^8 in probability, or a row meets its first visible key. Otherwise P <= 256, exact
-    // arithmetic on both sides of the final a / l. A fully masked tile never raises the reference,
-    // so visiting it (no-skip mode) changes nothing.
-    const bool need = (m_run == -INFINITY) ? (mx != -INFINITY) : ((mx - m_run) * c > kLazyLog2);
-    const bool raise = __any(need);
-    const float m_new = raise ? fmaxf(m_run, mx) : m_run;
-    const float ms_new = (m_new == -INFINITY) ? 0.0f : m_new * c;
-    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < 10; ++i) t1[i] = max3(r[3 * i], r[3 * i + 1], r[3 * i + 2]);
+    t1[10] = r[30];
+    t1[11] = r[31];
+    const float t2a = max3(t1[0], t1[1], t1[2]);
+    const float t2b = max3(t1[3], t1[4], t1[5]);
+    const float t2c = max3(t1[6], t1[7], t1[8]);
+    const float t2d = max3(t1[9], t1[10], t1[11]);
+    const float mx = max_with_partner_half(max3(t2a, t2b, max2(t2c, t2d))) * c;
+    // Lazy rescaling: the reference is raised (and the accumulators rescaled) only when some
+    // row's tile maximum exceeds it by more than 2^8 in probability, or a row meets its first
+    // visible key (mx - mref = +inf); otherwise P <= 256, exact arithmetic on both sides of the
+    // final a / l. A row that has seen nothing yet and sees nothing here gives -inf - -inf = NaN,
+    // which compares false: a fully masked tile never raises, so visiting it changes nothing.
+    const bool raise = __any((mx - mref) > kLazyLog2);
+    const float mnew = raise ? max2(mref, mx) : mref;
+    const float msub_new = (mnew == -INFINITY) ? 0.0f : mnew;
+    // P in bf16 pairs; the row sum is taken over the rounded values (the weights that multiply
+    // V), one dot product with (1, 1) per pair in four independent chains. The operand is
+    // assembled from whole 32-bit pairs: extracting pairs back out of the bf16x8 vector is
+    // mis-lowered by the compiler.
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
+    for (int q4 = 0; q4 < 4; ++q4) {
+      u32x4 w;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(r[8 * q4 + t], c, -ms_new));
-        ps[t & 3] += e;
-        pb[q4][t] = (__bf16)e;
+      for (int i = 0; i < 4; ++i) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(r[8 * q4 + 2 * i], c, -msub_new));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(r[8 * q4 + 2 * i + 1], c, -msub_new));
+        const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+        ls[i] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, ls[i], false);
+        w[i] = __builtin_bit_cast(unsigned, pr);
       }
-    const float lsum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      pb[q4] = __builtin_bit_cast(bf16x8, w);
+    }
+    const float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     if (raise) {
       // the accumulator gets this tile's P.V next; rescale it to the raised reference first
-      const float ms_old = (m_run == -INFINITY) ? -INFINITY : m_run * c;
-      const float alpha = __builtin_amdgcn_exp2f(ms_old - ms_new);
+      // (a row still without keys keeps alpha = 1: its accumulator and sum are zero)
+      const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref - mnew);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
       l_run *= alpha;
     }
-    m_run = m_new;
+    mref = mnew;
     l_run += lsum;
   };
 

@@ -46,6 +46,7 @@ def test_binding_constants_match_header(lib):
     defines, enum = header_defines()
     assert defines["PFA_NO_CAUSAL"] == pfa.NO_CAUSAL
     assert defines["PFA_FLAG_NO_SKIP"] == pfa.FLAG_NO_SKIP
+    assert defines["PFA_MAX_LEN"] == pfa.MAX_LEN
     assert defines["PFA_VERSION"] == pfa.version()
     assert {v: k for k, v in enum.items()} == pfa.STATUS
 
@@ -78,6 +79,7 @@ def call(**kw):
     (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1),
     (dict(B=0), 2), (dict(Hq=0), 2), (dict(Hkv=-1), 2), (dict(L=0), 2), (dict(S=0), 2), (dict(D=0), 2),
     (dict(B=2 ** 31 - 1, Hq=2 ** 31 - 1, L=2 ** 31 - 1, Hkv=1), 2),
+    (dict(S=2 ** 30 + 1), 2), (dict(L=2 ** 30 + 1), 2), (dict(S=2 ** 31 - 1), 2),
     (dict(Hq=6, Hkv=4), 3), (dict(Hq=7, Hkv=2), 3),
     (dict(D=96), 4), (dict(D=256), 4), (dict(D=32), 4),
     (dict(off=-1, window=5), 5),
