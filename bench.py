@@ -1,6 +1,8 @@
 """Throughput of grouped-query flash prefill attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --calibrate-copy     (three plain 1 GiB device copies: the reference kernel
+                                          that HBM byte counters are scaled against)
 
 A step is one pass of the prefill attention over one batch of each workload chunk, with all
 inputs resident in HBM before the timed region starts. The default workload is the pair of causal
@@ -131,6 +133,7 @@ def main() -> int:
     ap.add_argument("--workload", default="causal_8k_32k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this prefill-attention library has no multi-GPU path "
@@ -145,6 +148,15 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        a = torch.ones(2 ** 28, dtype=torch.int32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print("copied 3 x 1 GiB", flush=True)
+        return 0
     calls = []
     total_flops = 0
     per_cfg = []
@@ -229,7 +241,8 @@ def main() -> int:
         } for pc, ms in zip(per_cfg, mean_ms)],
         "roofline": {
             "bound": "mfma",
-            "kernel": "pfa_prefill_kernel<128,4>" if CONFIGS[WORKLOADS[args.workload][0]]["D"] == 128 else "pfa_prefill_kernel<64,4>",
+            "kernel": "pfa_prefill_kernel<%d,%s>" % (CONFIGS[WORKLOADS[args.workload][0]]["D"],
+                                                     "true" if CONFIGS[WORKLOADS[args.workload][0]]["key_padding"] else "false"),
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

@@ -23,11 +23,11 @@
 //    one VALU phase. Waves 0-3 and 4-7 run these phases in opposite halves of each iteration
 //    (two barriers per iteration), so on every SIMD one wave feeds the matrix core while the
 //    other runs the exponentials. In the MFMA phase each LDS operand is read three MFMAs ahead.
-//  * K/V tiles (64 keys x D) go from HBM straight into LDS with global_load_lds_dwordx4 (each
-//    instruction writes 1 KB of consecutive LDS), into one of three stages: tile t+1 lands while
-//    tile t's K and tile t-1's V are read. Rows are unpadded; 16-byte chunks are XOR-swizzled
-//    per row so both the K reads (ds_read_b128, one row per lane) and the V transpose reads
-//    (four rows per 16 lanes) are free of bank conflicts.
+//  * K/V tiles (64 keys x D) go from HBM straight into LDS with buffer_load_dwordx4 ... lds (each
+//    instruction writes 1 KB of consecutive LDS; waves 0-3 fetch K, waves 4-7 fetch V), into one
+//    of three stages: tile t+1 lands while tile t's K and tile t-1's V are read. Rows are
+//    unpadded; 16-byte chunks are XOR-swizzled per row so both the K reads (ds_read_b128, one row
+//    per lane) and the V transpose reads (four rows per 16 lanes) are free of bank conflicts.
 //  * Scores are scaled by scale*log2(e) inside the exp2 argument (one FMA per score).
 //  * The tile range of a workgroup is bounded by the causal and window edges; with a key mask a
 //    per-tile "any valid" bitmap (64 tiles per ballot) lets the loop jump over empty tiles; waves
