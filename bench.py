@@ -42,10 +42,13 @@ WORKLOADS = {
     "bidir_padded_b8": ["bidir_padded_b8"],
     "small_prompt_128": ["small_prompt_128"],
     "causal_witness_33x47": ["causal_witness_33x47"],
+    "varlen_causal_b8": ["varlen_causal_b8"],
 }
 DESCRIPTION = {
     "causal_8k_32k": "causal GQA prefill chunks, L=2048 on S=8192 (Hq=56,Hkv=8) and on S=32768 "
                      "(Hq=32,Hkv=8), D=128, one of each per step",
+    "varlen_causal_b8": "packed variable-length causal GQA prompt prefill, 8 sequences of 1024..4096 "
+                        "tokens (Lq == Lk), Hq=32, Hkv=8, D=128, one launch per step",
 }
 
 
@@ -62,6 +65,29 @@ def visible_pairs(c: dict, key_lengths=None) -> int:
         lo = max(0, i + off - W + 1) if W > 0 else 0
         total += max(0, hi - lo + 1)
     return B * Hq * total
+
+
+def varlen_visible_pairs(x: dict) -> int:
+    """Visible (row, key) cells over all query heads of a packed batch, closed form per row."""
+    import numpy as np
+
+    total = 0
+    for lq, lk in zip(x["lengths_q"], x["lengths_k"]):
+        i = np.arange(int(lq), dtype=np.int64)
+        if x["causal"]:
+            off = int(lk) - int(lq)
+            hi = np.minimum(int(lk) - 1, i + off)
+            lo = np.maximum(0, i + off - x["window"] + 1) if x["window"] > 0 else np.zeros_like(i)
+        else:
+            hi = np.full_like(i, int(lk) - 1)
+            lo = np.zeros_like(i)
+        total += int(np.maximum(0, hi - lo + 1).sum())
+    return total * x["Hq"]
+
+
+def varlen_algorithmic_bytes(x: dict) -> int:
+    D = x["D"]
+    return 2 * (2 * x["total_q"] * x["Hq"] * D + 2 * x["total_k"] * x["Hkv"] * D) + 8 * (x["n_seq"] + 1)
 
 
 def algorithmic_bytes(c: dict) -> int:
@@ -87,6 +113,14 @@ def recorded_traffic(workload: str):
     return float(val.group(1))
 
 
+def blas_single_thread():
+    """Context that pins the BLAS library to one thread per calling thread, so that `cores` is the
+    number of worker threads actually used."""
+    from threadpoolctl import threadpool_limits
+
+    return threadpool_limits(limits=1, user_api="blas")
+
+
 def cpu_baseline(workers: int, budget_s: float = 20.0) -> dict:
     """The oracle as it stands, on a bounded sample of the 8K chunk: heads taken one by one (all
     2048 rows each) until about `budget_s` of wall time has passed."""
@@ -100,6 +134,8 @@ def cpu_baseline(workers: int, budget_s: float = 20.0) -> dict:
     G = c["Hq"] // c["Hkv"]
     per_head_pairs = visible_pairs(dict(c, B=1, Hq=1))
     heads = 0
+    limit = blas_single_thread()
+    limit.__enter__()
     t0 = time.perf_counter()
     step = max(1, workers // 8)
     while time.perf_counter() - t0 < budget_s and heads < c["Hq"]:
@@ -118,11 +154,56 @@ def cpu_baseline(workers: int, budget_s: float = 20.0) -> dict:
             oracle_sdpa(q, k, v, x["scale"], c["causal_offset"], c["window"], None, workers=workers)
         heads = h1
     dt = time.perf_counter() - t0
+    limit.__exit__(None, None, None)
     flops = 4.0 * c["D"] * per_head_pairs * heads
     del np
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
             "sample": f"mid_ctx_8k (L=2048, S=8192, D=128): {heads} of {c['Hq']} query heads, all rows, "
-                      f"fp64 NumPy, {dt:.1f} s wall, {workers} threads"}
+                      f"fp64 NumPy, {dt:.1f} s wall, {workers} threads x 1 BLAS thread"}
+
+
+def kernel_name(workload_name: str) -> str:
+    from workloads import CONFIGS, VARLEN_CONFIGS
+
+    if workload_name in VARLEN_CONFIGS:
+        return "pfa_prefill_kernel<%d,false>" % VARLEN_CONFIGS[workload_name]["D"]
+    c = CONFIGS[workload_name]
+    return "pfa_prefill_kernel<%d,%s>" % (c["D"], "true" if c["key_padding"] else "false")
+
+
+def varlen_cpu_baseline(name: str, workers: int, budget_s: float = 20.0) -> dict:
+    """The varlen oracle as it stands, on a bounded sample of the packed workload: the first
+    sequence alone, its query heads one by one, until about `budget_s` of wall time has passed."""
+    import numpy as np
+
+    from oracle import oracle_varlen
+    from workloads import make_varlen_inputs
+
+    x = make_varlen_inputs(name, seed=0)
+    s0, s1 = int(x["cu_q"][0]), int(x["cu_q"][1])
+    k0, k1 = int(x["cu_k"][0]), int(x["cu_k"][1])
+    G = x["Hq"] // x["Hkv"]
+    one = dict(x, lengths_q=x["lengths_q"][:1], lengths_k=x["lengths_k"][:1], Hq=1)
+    per_head_flops = 4 * x["D"] * varlen_visible_pairs(one)
+    cu_q = np.array([0, s1 - s0], dtype=np.int32)
+    cu_k = np.array([0, k1 - k0], dtype=np.int32)
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one_head(h):
+        oracle_varlen(x["q"][s0:s1, h:h + 1], x["k"][k0:k1, h // G:h // G + 1], x["v"][k0:k1, h // G:h // G + 1],
+                      cu_q, cu_k, x["scale"], x["causal"], x["window"])
+
+    heads = 0
+    t0 = time.perf_counter()
+    with blas_single_thread(), ThreadPoolExecutor(max_workers=workers) as ex:
+        while time.perf_counter() - t0 < budget_s and heads < x["Hq"]:
+            h1 = min(x["Hq"], heads + workers)
+            list(ex.map(one_head, range(heads, h1)))
+            heads = h1
+    dt = time.perf_counter() - t0
+    return {"value": per_head_flops * heads / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"{name}: sequence 0 (Lq={s1 - s0}, Lk={k1 - k0}), {heads} of {x['Hq']} query heads, "
+                      f"fp64 NumPy, {dt:.1f} s wall, {workers} threads x 1 BLAS thread"}
 
 
 def main() -> int:
@@ -144,7 +225,7 @@ def main() -> int:
     import torch
 
     import prefill_attention_amd as pfa
-    from workloads import CONFIGS, make_inputs
+    from workloads import CONFIGS, VARLEN_CONFIGS, make_inputs, make_varlen_inputs
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -160,12 +241,28 @@ def main() -> int:
     calls = []
     total_flops = 0
     per_cfg = []
+    def t(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
     for name in WORKLOADS[args.workload]:
+        if name in VARLEN_CONFIGS:
+            x = make_varlen_inputs(name, seed=0)
+            q, k, v = t(x["q"]), t(x["k"]), t(x["v"])
+            kw = dict(scale=float(x["scale"]), causal=x["causal"], window=x["window"], out=torch.empty_like(q))
+            cq = torch.from_numpy(x["cu_q"]).to(dev)
+            ck = torch.from_numpy(x["cu_k"]).to(dev)
+            mq = x["max_seqlen_q"]
+
+            def launch(q=q, k=k, v=v, cq=cq, ck=ck, mq=mq, kw=kw):
+                pfa.prefill_attn_gqa_varlen(q, k, v, cq, ck, mq, **kw)
+
+            flops = 4 * x["D"] * varlen_visible_pairs(x)
+            total_flops += flops
+            calls.append((name, launch))
+            per_cfg.append(dict(name=name, flops=flops, rows=x["total_q"], bytes=varlen_algorithmic_bytes(x)))
+            continue
         c = CONFIGS[name]
         x = make_inputs(name, seed=0)
-
-        def t(bits):
-            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
         q, k, v = t(x["q"]), t(x["k"]), t(x["v"])
         m = torch.from_numpy(x["key_mask"]).to(dev) if x["key_mask"] is not None else None
@@ -176,15 +273,19 @@ def main() -> int:
                   key_mask=m, out=out)
         flops = 4 * c["D"] * visible_pairs(c, x["key_lengths"])
         total_flops += flops
-        calls.append((name, q, k, v, kw))
+
+        def launch(q=q, k=k, v=v, kw=kw):
+            pfa.prefill_attn_gqa(q, k, v, **kw)
+
+        calls.append((name, launch))
         per_cfg.append(dict(name=name, flops=flops, rows=c["B"] * c["L"], bytes=algorithmic_bytes(c)))
     torch.cuda.synchronize()
 
     def step(events=None):
-        for idx, (name, q, k, v, kw) in enumerate(calls):
+        for idx, (name, launch) in enumerate(calls):
             if events is not None:
                 events[idx][0].record()
-            pfa.prefill_attn_gqa(q, k, v, **kw)
+            launch()
             if events is not None:
                 events[idx][1].record()
 
@@ -229,7 +330,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload,
                    "description": DESCRIPTION.get(args.workload, args.workload),
-                   "chunks": [CONFIGS[n] | {"name": n} for n in WORKLOADS[args.workload]]},
+                   "chunks": [(CONFIGS.get(n) or VARLEN_CONFIGS[n]) | {"name": n} for n in WORKLOADS[args.workload]]},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "per_workload": [{
             "name": pc["name"],
@@ -241,8 +342,7 @@ def main() -> int:
         } for pc, ms in zip(per_cfg, mean_ms)],
         "roofline": {
             "bound": "mfma",
-            "kernel": "pfa_prefill_kernel<%d,%s>" % (CONFIGS[WORKLOADS[args.workload][0]]["D"],
-                                                     "true" if CONFIGS[WORKLOADS[args.workload][0]]["key_padding"] else "false"),
+            "kernel": kernel_name(WORKLOADS[args.workload][0]),
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -255,7 +355,10 @@ def main() -> int:
     if not args.no_cpu_baseline:
         from oracle import host_workers
         workers = min(16, host_workers())
-        rec["cpu_baseline"] = cpu_baseline(workers, args.cpu_budget)
+        if args.workload == "varlen_causal_b8":
+            rec["cpu_baseline"] = varlen_cpu_baseline(args.workload, workers, args.cpu_budget)
+        else:
+            rec["cpu_baseline"] = cpu_baseline(workers, args.cpu_budget)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define PFA_VERSION 10000 /* 1.0.0 */
+#define PFA_VERSION 10100 /* 1.1.0 */
 
 /* causal_offset < 0 selects bidirectional attention (no causal term). */
 #define PFA_NO_CAUSAL (-1)
@@ -59,14 +59,14 @@ extern "C" {
 
 enum pfa_status {
   PFA_OK = 0,
-  PFA_ERR_NULL = 1,      /* Q, K, V or O is NULL                                               */
+  PFA_ERR_NULL = 1,      /* Q, K, V, O (or a varlen prefix-sum buffer) is NULL                 */
   PFA_ERR_SIZE = 2,      /* a size < 1, L or S > PFA_MAX_LEN, or a size product / grid too big  */
   PFA_ERR_GQA = 3,       /* Hq is not a multiple of Hkv                                         */
   PFA_ERR_HEAD_DIM = 4,  /* D is not 64 or 128                                                  */
   PFA_ERR_MASK_ARGS = 5, /* window > 0 without the causal term                                  */
   PFA_ERR_SCALE = 6,     /* scale is not finite or not > 0                                      */
-  PFA_ERR_ALIGN = 7,     /* Q, K, V or O is not 16-byte aligned                                 */
-  PFA_ERR_ALIAS = 8,     /* O overlaps Q, K, V or key_mask                                      */
+  PFA_ERR_ALIGN = 7,     /* Q, K, V or O not 16-byte aligned (prefix sums: not 4-byte aligned)  */
+  PFA_ERR_ALIAS = 8,     /* O overlaps Q, K, V, key_mask or a prefix-sum buffer                 */
   PFA_ERR_FLAGS = 9,     /* unknown bit in flags                                                */
   PFA_ERR_LAUNCH = 10    /* the HIP launch failed (e.g. no gfx950 device is current)            */
 };
@@ -106,6 +106,45 @@ int prefill_attn_gqa_ex(const void* Q, const void* K, const void* V,
                         float scale, int causal_offset, int window,
                         const uint8_t* key_mask, void* O, void* stream,
                         unsigned flags);
+
+/*
+ * prefill_attn_gqa_varlen -- the same attention over a packed batch of variable-length sequences
+ * (brotensor flash_attention.h, flash_attention_varlen_forward: all sequences live back to back
+ * in one packed tensor, sequence boundaries come from INT32 prefix-sum buffers of n_seq + 1
+ * entries, and no query attends to a key of another sequence).
+ *
+ *   Q, O          bf16 [total_q, Hq, D]   token-major: the rows of all sequences back to back,
+ *                                        the Hq heads of one row contiguous
+ *   K, V          bf16 [total_k, Hkv, D]  same packing for the keys (grouped-query heads as in
+ *                                        prefill_attn_gqa: query head h reads KV head h / (Hq/Hkv))
+ *   cu_seqlens_q  DEVICE int32 [n_seq + 1]: sequence b owns query rows
+ *                 [cu_seqlens_q[b], cu_seqlens_q[b+1])
+ *   cu_seqlens_k  DEVICE int32 [n_seq + 1]: sequence b owns keys [cu_seqlens_k[b], cu_seqlens_k[b+1])
+ *                 Both must start at 0, be non-decreasing and end at total_q / total_k. They are
+ *                 read only by the kernel (the host never dereferences them); every bound is
+ *                 clamped into [0, total], so malformed sums cannot cause an out-of-bounds access
+ *                 (the result is then unspecified).
+ *   n_seq         number of sequences (>= 1); a sequence may have no rows or no keys
+ *   max_seqlen_q  largest per-sequence query length (>= 1, <= PFA_MAX_LEN); the grid covers this
+ *                 many rows per sequence, rows past it are not computed
+ *   total_q, total_k  packed row counts (>= 1)
+ *   Hq, Hkv, D, scale  as in prefill_attn_gqa
+ *   causal        nonzero: local row i of sequence b sees local keys j <= i + (Lk_b - Lq_b), the
+ *                 lower-right alignment of a chunk that follows its cached keys; for Lq_b == Lk_b
+ *                 this is the page's rule j <= i. A row with no visible key gets zeros.
+ *   window        > 0: also j >= i + (Lk_b - Lq_b) - window + 1; requires causal
+ *   O             fully overwritten for well-formed prefix sums
+ *   stream        hipStream_t to enqueue on; NULL = the default stream
+ *
+ * Each sequence is computed exactly as prefill_attn_gqa computes it alone (same key-tile grid
+ * anchored at the sequence's first key), so the result for a sequence is bit-identical to the
+ * dense call on that sequence. Returns a pfa_status code.
+ */
+int prefill_attn_gqa_varlen(const void* Q, const void* K, const void* V,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int n_seq, int max_seqlen_q, int total_q, int total_k,
+                            int Hq, int Hkv, int D, float scale, int causal, int window,
+                            void* O, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* pfa_status_str(int status);

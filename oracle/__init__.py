@@ -16,3 +16,4 @@ from .sdpa import (  # noqa: F401
     visible,
     visible_pair_count,
 )
+from .varlen import oracle_varlen, oracle_varlen_rows, varlen_visible  # noqa: F401

@@ -13,6 +13,8 @@ from ._binding import (  # noqa: F401
     library,
     prefill_attn_gqa,
     prefill_attn_gqa_raw,
+    prefill_attn_gqa_varlen,
+    prefill_attn_gqa_varlen_raw,
     status_str,
     version,
 )

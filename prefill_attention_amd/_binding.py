@@ -22,7 +22,8 @@ STATUS = {
     5: "PFA_ERR_MASK_ARGS", 6: "PFA_ERR_SCALE", 7: "PFA_ERR_ALIGN", 8: "PFA_ERR_ALIAS",
     9: "PFA_ERR_FLAGS", 10: "PFA_ERR_LAUNCH",
 }
-EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "pfa_status_str", "pfa_version")
+EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_varlen", "pfa_status_str",
+           "pfa_version")
 
 _lib = None
 
@@ -48,6 +49,9 @@ def library() -> ctypes.CDLL:
         lib.prefill_attn_gqa.restype = ci
         lib.prefill_attn_gqa_ex.argtypes = sig + [cu]
         lib.prefill_attn_gqa_ex.restype = ci
+        lib.prefill_attn_gqa_varlen.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, ci,
+                                                vp, vp]
+        lib.prefill_attn_gqa_varlen.restype = ci
         lib.pfa_status_str.argtypes = [ci]
         lib.pfa_status_str.restype = ctypes.c_char_p
         lib.pfa_version.argtypes = []
@@ -139,6 +143,68 @@ def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True
         rc = prefill_attn_gqa_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
                                   float(scale), int(causal_offset), int(window), mask_ptr,
                                   out.data_ptr(), stream_ptr, FLAG_NO_SKIP if no_skip else 0)
+    if rc != 0:
+        raise PfaError(rc, status_str(rc))
+    return out
+
+
+def prefill_attn_gqa_varlen_raw(q_ptr: int, k_ptr: int, v_ptr: int, cu_q_ptr: int, cu_k_ptr: int,
+                                n_seq: int, max_seqlen_q: int, total_q: int, total_k: int, Hq: int,
+                                Hkv: int, D: int, scale: float, causal: bool, window: int,
+                                o_ptr: int, stream: int | None) -> int:
+    """Direct C-ABI call of the packed variable-length entry point; returns the status code."""
+    return int(library().prefill_attn_gqa_varlen(
+        q_ptr, k_ptr, v_ptr, cu_q_ptr, cu_k_ptr, n_seq, max_seqlen_q, total_q, total_k, Hq, Hkv, D,
+        ctypes.c_float(scale), 1 if causal else 0, window, o_ptr, stream or None))
+
+
+def prefill_attn_gqa_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *,
+                            scale: float | None = None, causal: bool = True, window: int = 0,
+                            out=None, stream=None):
+    """Packed variable-length grouped-query attention on torch tensors.
+
+    q: bf16 [total_q, Hq, D]; k, v: bf16 [total_k, Hkv, D]; cu_seqlens_q / cu_seqlens_k: int32
+    [n_seq + 1] prefix sums on the same device. max_seqlen_q bounds every sequence's query
+    length. With causal=True local row i of a sequence sees local keys j <= i + (Lk - Lq).
+    Returns `out` (allocated if None), bf16 [total_q, Hq, D].
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 3-D bfloat16 GPU tensor")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.dim() != 1
+                or not t.is_contiguous() or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous 1-D int32 tensor on {q.device}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+    total_q, Hq, D = q.shape
+    total_k, Hkv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Dk != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    n_seq = cu_seqlens_q.numel() - 1
+    if n_seq < 1 or cu_seqlens_k.numel() != n_seq + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have n_seq + 1 >= 2 entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if window > 0 and not causal:
+        raise ValueError("a sliding window needs causal=True")
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    stream_ptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        rc = prefill_attn_gqa_varlen_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
+                                         cu_seqlens_k.data_ptr(), n_seq, int(max_seqlen_q), total_q, total_k,
+                                         Hq, Hkv, D, float(scale), bool(causal), int(window), out.data_ptr(),
+                                         stream_ptr)
     if rc != 0:
         raise PfaError(rc, status_str(rc))
     return out

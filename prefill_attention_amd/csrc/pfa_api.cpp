@@ -88,6 +88,7 @@ int prefill_attn_gqa_ex(const void* Q, const void* K, const void* V, int B, int 
   p.sk = S;
   p.d = D;
   p.scale = scale;
+  p.causal = causal_offset >= 0 ? 1 : 0;
   p.causal_offset = causal_offset < 0 ? PFA_NO_CAUSAL : causal_offset;
   p.window = (causal_offset >= 0 && window > 0) ? window : 0;
   p.flags = flags;
@@ -103,10 +104,69 @@ int prefill_attn_gqa(const void* Q, const void* K, const void* V, int B, int Hq,
                              key_mask, O, stream, 0u);
 }
 
+int prefill_attn_gqa_varlen(const void* Q, const void* K, const void* V,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seq,
+                            int max_seqlen_q, int total_q, int total_k, int Hq, int Hkv, int D,
+                            float scale, int causal, int window, void* O, void* stream) {
+  if (!Q || !K || !V || !O || !cu_seqlens_q || !cu_seqlens_k) return PFA_ERR_NULL;
+  if (n_seq < 1 || max_seqlen_q < 1 || total_q < 1 || total_k < 1 || Hq < 1 || Hkv < 1 || D < 1)
+    return PFA_ERR_SIZE;
+  if (max_seqlen_q > PFA_MAX_LEN || n_seq == INT_MAX) return PFA_ERR_SIZE;
+  // packed row strides (Hq * D, Hkv * D elements) and a 64-key tile's byte extent stay in 31 bits
+  if (Hq > (1 << 24) / 128 || Hkv > (1 << 24) / 128) return PFA_ERR_SIZE;
+  const long long lim = LLONG_MAX / 4;
+  long long q_elems, kv_elems, t;
+  if (!mul_fits(total_q, Hq, lim, &t) || !mul_fits(t, D, lim, &q_elems)) return PFA_ERR_SIZE;
+  if (!mul_fits(total_k, Hkv, lim, &t) || !mul_fits(t, D, lim, &kv_elems)) return PFA_ERR_SIZE;
+  if (Hq % Hkv != 0) return PFA_ERR_GQA;
+  if (D != 64 && D != 128) return PFA_ERR_HEAD_DIM;
+  if (window > 0 && !causal) return PFA_ERR_MASK_ARGS;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return PFA_ERR_SCALE;
+  const uintptr_t a16 = 15, a4 = 3;
+  if ((reinterpret_cast<uintptr_t>(Q) & a16) || (reinterpret_cast<uintptr_t>(K) & a16) ||
+      (reinterpret_cast<uintptr_t>(V) & a16) || (reinterpret_cast<uintptr_t>(O) & a16) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_q) & a4) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & a4))
+    return PFA_ERR_ALIGN;
+  const auto range = [](const void* p, long long bytes) {
+    return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + static_cast<uintptr_t>(bytes)};
+  };
+  const Range o = range(O, q_elems * 2);
+  const long long cu_bytes = (static_cast<long long>(n_seq) + 1) * 4;
+  if (overlaps(o, range(Q, q_elems * 2)) || overlaps(o, range(K, kv_elems * 2)) ||
+      overlaps(o, range(V, kv_elems * 2)) || overlaps(o, range(cu_seqlens_q, cu_bytes)) ||
+      overlaps(o, range(cu_seqlens_k, cu_bytes)))
+    return PFA_ERR_ALIAS;
+  pfa::Launch p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.key_mask = nullptr;
+  p.o = O;
+  p.batch = n_seq;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.group = Hq / Hkv;
+  p.lq = max_seqlen_q;
+  p.sk = 0;
+  p.d = D;
+  p.scale = scale;
+  p.causal = causal ? 1 : 0;
+  p.causal_offset = 0;  // per sequence: Lk - Lq
+  p.window = (causal && window > 0) ? window : 0;
+  p.flags = 0;
+  p.stream = stream;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  if (pfa::grid_blocks(p) > INT_MAX) return PFA_ERR_SIZE;
+  return pfa::launch_prefill(p);
+}
+
 const char* pfa_status_str(int status) {
   switch (status) {
     case PFA_OK: return "ok";
-    case PFA_ERR_NULL: return "null tensor pointer (Q, K, V and O are required)";
+    case PFA_ERR_NULL: return "null pointer (Q, K, V, O and, for varlen, both prefix sums are required)";
     case PFA_ERR_SIZE: return "invalid size: B, Hq, Hkv, L, S, D must be >= 1 and fit the launch";
     case PFA_ERR_GQA: return "Hq must be a multiple of Hkv";
     case PFA_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";

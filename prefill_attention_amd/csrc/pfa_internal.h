@@ -15,10 +15,17 @@ struct Launch {
   void* o;
   int batch, hq, hkv, group, lq, sk, d;
   float scale;
-  int causal_offset;        // < 0: no causal term
+  int causal;               // causal term on
+  int causal_offset;        // dense layout: row i sees keys j <= i + causal_offset (if causal)
   int window;               // > 0 only with the causal term
   unsigned flags;
   void* stream;
+  // Packed variable-length layout (both null for the dense layout): batch is the number of
+  // sequences, lq the largest query length the grid covers, cu_q / cu_k the device prefix sums
+  // (batch + 1 entries each), total_q / total_k the packed row counts.
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int total_q = 0, total_k = 0;
 };
 
 // Query rows handled by one workgroup of the prefill kernel.

@@ -95,8 +95,16 @@ struct Params {
   uint16_t* o;
   int hq, hkv, group, lq, sk;
   float c;  // scale * log2(e)
+  int causal;         // causal term on
   int causal_offset, window;
+  // Packed variable-length batches (null for the dense layout): sequence b owns query rows
+  // [cu_q[b], cu_q[b+1]) of the packed [total_q, Hq, D] Q / O and keys [cu_k[b], cu_k[b+1]) of
+  // the packed [total_k, Hkv, D] K / V; the causal offset is taken per sequence (Lk - Lq).
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
   int no_skip;
+  int batch;
   int n_qblk;
   int n_wg;
   int xcd_remap;
@@ -194,25 +202,57 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   const int hh = lane >> 5;
   const bool group_a = wave < 4;  // waves w and w+4 share a SIMD and take opposite phases
 
-  // ---- workgroup -> (b, kv head, query block, head in group) ----
+  // ---- workgroup -> (kv head, query-block rank, b, head in group) ----
+  // Items are numbered with the KV head slowest, so that (when the hardware deals workgroups to
+  // the 8 XCDs round-robin and blockIdx is remapped accordingly) every XCD holds whole KV heads of
+  // every batch element: the workgroups that share a K/V tile share an L2, and sequences of
+  // different lengths spread over all XCDs. Rank 0 is each sequence's heaviest causal block.
   int item = blockIdx.x;
   if (p.xcd_remap) item = (blockIdx.x % kXcds) * (p.n_wg / kXcds) + blockIdx.x / kXcds;
   const int g = item % p.group;
   item /= p.group;
+  const int b = item % p.batch;
+  item /= p.batch;
   const int qrank = item % p.n_qblk;
-  item /= p.n_qblk;
-  const int hk = item % p.hkv;
-  const int b = item / p.hkv;
-  const bool causal = p.causal_offset >= 0;
-  const int qblk = causal ? (p.n_qblk - 1 - qrank) : qrank;
+  const int hk = item / p.n_qblk;
+  const bool causal = p.causal != 0;
   const int h = hk * p.group + g;
-  const int L = p.lq, S = p.sk;
+  // Rows and keys of this workgroup's sequence, their base elements and strides. Dense layout:
+  // [B, H, L|S, D] (row stride D). Packed layout: [total, H, D] (row stride H * D), with the
+  // sequence bounds clamped to the packed extents so that malformed prefix sums stay in bounds.
+  int L, S, causal_offset;
+  long long q_base, kv_base;
+  int q_stride, kv_stride;
+  if (p.cu_q == nullptr) {
+    L = p.lq;
+    S = p.sk;
+    causal_offset = p.causal_offset;
+    q_base = ((long long)b * p.hq + h) * (long long)L * D;
+    kv_base = ((long long)b * p.hkv + hk) * (long long)S * D;
+    q_stride = D;
+    kv_stride = D;
+  } else {
+    const int qs = min(max(p.cu_q[b], 0), p.total_q);
+    const int qe = min(max(p.cu_q[b + 1], qs), p.total_q);
+    const int ks = min(max(p.cu_k[b], 0), p.total_k);
+    const int ke = min(max(p.cu_k[b + 1], ks), p.total_k);
+    L = min(qe - qs, p.lq);  // p.lq holds the largest sequence length the grid covers
+    S = ke - ks;
+    causal_offset = S - L;
+    q_base = ((long long)qs * p.hq + h) * D;
+    kv_base = ((long long)ks * p.hkv + hk) * D;
+    q_stride = p.hq * D;
+    kv_stride = p.hkv * D;
+  }
   const int W = p.window;
+  const int nb = (L + kBM - 1) / kBM;  // query blocks of this sequence
+  if (qrank >= nb) return;  // past the end of a shorter sequence: the whole workgroup leaves
+  const int qblk = causal ? (nb - 1 - qrank) : qrank;
   const int q0 = qblk * kBM;
   const int q1 = (q0 + kBM) < L ? (q0 + kBM) : L;
 
-  const uint16_t* kg = p.k + ((long long)b * p.hkv + hk) * (long long)S * D;
-  const uint16_t* vg = p.v + ((long long)b * p.hkv + hk) * (long long)S * D;
+  const uint16_t* kg = p.k + kv_base;
+  const uint16_t* vg = p.v + kv_base;
   const uint8_t* mrow = KMASK ? p.key_mask + (long long)b * S : nullptr;
   constexpr bool kmask = KMASK;
 
@@ -220,11 +260,12 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   const int n_tiles = (S + kBN - 1) / kBN;
   int kt_lo = 0, kt_hi = n_tiles;
   if (!p.no_skip && causal) {
-    long long hi_key = (long long)q1 + p.causal_offset;  // exclusive
+    long long hi_key = (long long)q1 + causal_offset;  // exclusive
     if (hi_key > S) hi_key = S;
+    if (hi_key < 0) hi_key = 0;
     kt_hi = (int)((hi_key + kBN - 1) / kBN);
     if (W > 0) {
-      long long lo_key = (long long)q0 + p.causal_offset - W + 1;
+      long long lo_key = (long long)q0 + causal_offset - W + 1;
       if (lo_key < 0) lo_key = 0;
       const long long t = lo_key / kBN;
       kt_lo = (int)(t < n_tiles ? t : n_tiles);
@@ -240,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   {
     const int row = qw0 + l32;
     if (row < L) {
-      const uint16_t* qrow = p.q + (((long long)b * p.hq + h) * L + row) * (long long)D;
+      const uint16_t* qrow = p.q + q_base + (long long)row * q_stride;
 #pragma unroll
       for (int kk = 0; kk < KQ; ++kk)
         qreg[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * hh);
@@ -309,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     const int row = i * G::kRowsPerDma + lane / G::kChunksPerRow;
     const int pch = lane % G::kChunksPerRow;
     const int sw = group_a ? G::swz_k(row) : G::swz_v(row);
-    dma_off[j] = (unsigned)(row * G::kRowBytes + 16 * (pch ^ sw));
+    dma_off[j] = (unsigned)(row * 2 * kv_stride + 16 * (pch ^ sw));
   }
   // wave-uniform values, made scalar explicitly (the compiler cannot see that tid >> 6 is)
   const uint16_t* dma_src = group_a ? kg : vg;
@@ -319,8 +360,8 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   auto issue = [&](int kt, int st) __attribute__((always_inline)) {
     const long long key0 = (long long)kt * kBN;
     const long long rows = (long long)S - key0;
-    const int nrec = (rows < kBN ? (int)rows : kBN) * G::kRowBytes;
-    const uintptr_t base = reinterpret_cast<uintptr_t>(dma_src + key0 * D);
+    const int nrec = (rows < kBN ? (int)rows : kBN) * 2 * kv_stride;
+    const uintptr_t base = reinterpret_cast<uintptr_t>(dma_src + key0 * kv_stride);
     // readfirstlane returns int: go through unsigned so the low word is not sign-extended
     const unsigned base_hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(base >> 32));
     const unsigned base_lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)base);
@@ -365,12 +406,12 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   // term dc is pinned at +256 and with no window dw at -256, i.e. no bound inside a tile.
   const int cbase = [&] {
     if (!causal) return S + 512;
-    const long long t = (long long)p.causal_offset + qw0;
+    const long long t = (long long)causal_offset + qw0;
     return (int)(t < -512 ? -512 : (t > (long long)S + 512 ? (long long)S + 512 : t));
   }();
   const int wbase = [&] {
     if (!causal || W <= 0) return -512;
-    const long long t = (long long)p.causal_offset - W + 1 + qw0;
+    const long long t = (long long)causal_offset - W + 1 + qw0;
     return (int)(t < -512 ? -512 : (t > (long long)S + 512 ? (long long)S + 512 : t));
   }();
   auto view_of = [&](int kt, bool tile_all_valid) __attribute__((always_inline)) -> TileView {
@@ -620,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   const int row = qw0 + l32;
   if (row >= L) return;
-  uint16_t* orow = p.o + (((long long)b * p.hq + h) * L + row) * (long long)D;
+  uint16_t* orow = p.o + q_base + (long long)row * q_stride;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -647,9 +688,15 @@ int launch_variant(const pfa::Launch& L) {
   p.lq = L.lq;
   p.sk = L.sk;
   p.c = L.scale * kLog2e;
+  p.causal = L.causal;
   p.causal_offset = L.causal_offset;
+  p.cu_q = L.cu_q;
+  p.cu_k = L.cu_k;
+  p.total_q = L.total_q;
+  p.total_k = L.total_k;
   p.window = L.window;
   p.no_skip = (L.flags & PFA_FLAG_NO_SKIP) ? 1 : 0;
+  p.batch = L.batch;
   p.n_qblk = (L.lq + kBM - 1) / kBM;
   const long long n = (long long)L.batch * L.hq * p.n_qblk;
   p.n_wg = (int)n;

@@ -130,3 +130,51 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _binding.library()
+
+
+# ---- packed variable-length entry point ----
+CQ, CK = 6 * A, 7 * A
+VGOOD = dict(q=Q, k=K, v=V, cq=CQ, ck=CK, n=3, maxq=40, tq=100, tk=120, Hq=4, Hkv=2, D=128,
+             scale=0.088, causal=1, window=0, o=O, stream=None)
+
+
+def vcall(**kw):
+    a = dict(VGOOD)
+    a.update(kw)
+    return pfa.prefill_attn_gqa_varlen_raw(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["n"], a["maxq"],
+                                           a["tq"], a["tk"], a["Hq"], a["Hkv"], a["D"], a["scale"],
+                                           a["causal"], a["window"], a["o"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1), (dict(cq=0), 1), (dict(ck=0), 1),
+    (dict(n=0), 2), (dict(maxq=0), 2), (dict(tq=0), 2), (dict(tk=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2),
+    (dict(D=0), 2), (dict(maxq=2 ** 30 + 1), 2), (dict(n=2 ** 31 - 1), 2),
+    (dict(Hq=2 ** 18, Hkv=2 ** 18), 2),
+    (dict(maxq=2 ** 30, n=2 ** 20, Hq=64, Hkv=64), 2),
+    (dict(Hq=6, Hkv=4), 3),
+    (dict(D=96), 4),
+    (dict(causal=0, window=8), 5),
+    (dict(scale=float("nan")), 6), (dict(scale=0.0), 6),
+    (dict(q=Q + 8), 7), (dict(o=O + 2), 7), (dict(cq=CQ + 2), 7), (dict(ck=CK + 1), 7),
+    (dict(o=Q), 8), (dict(o=K + 16), 8), (dict(o=V), 8), (dict(cq=O + 4), 8), (dict(ck=O + 100 * 4 * 128 * 2 - 4), 8),
+], ids=lambda x: str(x))
+def test_varlen_invalid_arguments_rejected(lib, kw, code):
+    assert vcall(**kw) == code
+
+
+def test_varlen_prefix_sums_adjacent_to_o_are_not_alias(lib):
+    # cu buffers may sit right after O ([O, O + total_q*Hq*D*2) is half-open); the first error after
+    # the alias check is the launch, which needs a GPU, so only the alias code is ruled out
+    o_bytes = 100 * 4 * 128 * 2
+    rc = vcall(cq=O + o_bytes, ck=O + o_bytes + 16)
+    assert rc != 8
+
+
+def test_varlen_binding_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(10, 4, 128, dtype=torch.bfloat16)
+    k = torch.zeros(12, 2, 128, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 10], dtype=torch.int32)
+    with pytest.raises(ValueError, match="3-D bfloat16 GPU"):
+        pfa.prefill_attn_gqa_varlen(q, k, k, cu, cu, 10)

@@ -99,3 +99,56 @@ def random_bits(rng: np.random.Generator, shape, amp: float = 1.0) -> np.ndarray
     if amp != 1.0:
         x *= np.float32(amp)
     return f32_to_bf16_bits(x)
+
+
+# ----------------------------------------------------------------------------------------------
+# Packed variable-length batches (brotensor flash_attention_varlen_forward layout)
+# ----------------------------------------------------------------------------------------------
+# name -> workload. Query lengths are drawn from `lq` (inclusive range); each sequence's keys are
+# its cached prefix (drawn from `prefix`, inclusive) followed by its query rows, so Lk = prefix + Lq.
+VARLEN_CONFIGS: dict[str, dict] = {
+    # Batched causal prompt prefill, 8 packed sequences of 1024..4096 tokens (the key-padding
+    # workload's length mix, packed instead of padded), Lq == Lk.
+    "varlen_causal_b8": dict(n_seq=8, Hq=32, Hkv=8, D=128, lq=(1024, 4096), prefix=(0, 0), causal=True,
+                             window=0),
+    # Ragged chunks after cached prefixes: short and long rows, several key tiles, ragged tails.
+    "varlen_chunks_b5": dict(n_seq=5, Hq=8, Hkv=2, D=128, lq=(1, 300), prefix=(0, 500), causal=True,
+                             window=0),
+}
+
+
+def make_varlen_inputs(cfg: dict | str, seed: int = 0, lengths_q=None, lengths_k=None, **overrides) -> dict:
+    """Draw one packed variable-length workload.
+
+    Draw order from ``numpy.random.default_rng(seed)``: the n_seq query lengths, the n_seq prefix
+    lengths, then Q [total_q, Hq, D], K and V [total_k, Hkv, D] as float32 standard normals rounded
+    to bf16. ``lengths_q`` / ``lengths_k`` override the drawn lengths (the draws still happen, so the
+    value stream is the same). Returns bit arrays, int32 prefix sums ``cu_q`` / ``cu_k`` and the
+    arguments."""
+    if isinstance(cfg, str):
+        cfg = VARLEN_CONFIGS[cfg]
+    c = dict(cfg)
+    c.update(overrides)
+    n, Hq, Hkv, D = (int(c[k]) for k in ("n_seq", "Hq", "Hkv", "D"))
+    rng = np.random.default_rng(seed)
+    lq = rng.integers(c["lq"][0], c["lq"][1] + 1, size=n)
+    pre = rng.integers(c["prefix"][0], c["prefix"][1] + 1, size=n)
+    lk = lq + pre
+    if lengths_q is not None:
+        lq = np.asarray(lengths_q, dtype=np.int64)
+    if lengths_k is not None:
+        lk = np.asarray(lengths_k, dtype=np.int64)
+    n = len(lq)
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    q = rng.standard_normal((tq, Hq, D), dtype=np.float32)
+    k = rng.standard_normal((tk, Hkv, D), dtype=np.float32)
+    v = rng.standard_normal((tk, Hkv, D), dtype=np.float32)
+    return dict(
+        q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k), v=f32_to_bf16_bits(v),
+        cu_q=cu_q, cu_k=cu_k, lengths_q=lq.astype(np.int64), lengths_k=lk.astype(np.int64),
+        n_seq=n, Hq=Hq, Hkv=Hkv, D=D, total_q=tq, total_k=tk, max_seqlen_q=int(max(1, lq.max(initial=1))),
+        scale=np.float32(1.0 / np.sqrt(np.float32(D))), causal=bool(c.get("causal", True)),
+        window=int(c.get("window", 0)),
+    )
