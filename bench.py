@@ -43,6 +43,9 @@ WORKLOADS = {
     "small_prompt_128": ["small_prompt_128"],
     "causal_witness_33x47": ["causal_witness_33x47"],
     "varlen_causal_b8": ["varlen_causal_b8"],
+    "decode_l1_32k": ["decode_l1_32k"],
+    "decode_l8_8k": ["decode_l8_8k"],
+    "decode_b8_l1_4k": ["decode_b8_l1_4k"],
 }
 DESCRIPTION = {
     "causal_8k_32k": "causal GQA prefill chunks, L=2048 on S=8192 (Hq=56,Hkv=8) and on S=32768 "
@@ -168,6 +171,9 @@ def kernel_name(workload_name: str) -> str:
     if workload_name in VARLEN_CONFIGS:
         return "pfa_prefill_kernel<%d,false>" % VARLEN_CONFIGS[workload_name]["D"]
     c = CONFIGS[workload_name]
+    if c.get("entry") == "decode":
+        return "pfa_decode_split_kernel<%d,%d,%s> + pfa_decode_merge_kernel<%d>" % (
+            c["D"], 2 if (c["Hq"] // c["Hkv"]) * c["L"] > 32 else 1, "true" if c["key_padding"] else "false", c["D"])
     return "pfa_prefill_kernel<%d,%s>" % (c["D"], "true" if c["key_padding"] else "false")
 
 
@@ -271,11 +277,16 @@ def main() -> int:
         kw = dict(scale=float(x["scale"]), causal=causal,
                   causal_offset=x["causal_offset"] if causal else None, window=x["window"],
                   key_mask=m, out=out)
+        if c.get("entry") == "decode":
+            kw["workspace"] = torch.empty(pfa.decode_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["S"], c["D"]),
+                                          dtype=torch.uint8, device=dev)
         flops = 4 * c["D"] * visible_pairs(c, x["key_lengths"])
         total_flops += flops
 
-        def launch(q=q, k=k, v=v, kw=kw):
-            pfa.prefill_attn_gqa(q, k, v, **kw)
+        fn = pfa.prefill_attn_gqa_decode if c.get("entry") == "decode" else pfa.prefill_attn_gqa
+
+        def launch(q=q, k=k, v=v, kw=kw, fn=fn):
+            fn(q, k, v, **kw)
 
         calls.append((name, launch))
         per_cfg.append(dict(name=name, flops=flops, rows=c["B"] * c["L"], bytes=algorithmic_bytes(c)))
@@ -352,6 +363,22 @@ def main() -> int:
             "useful_flops_per_launch": total_flops / len(calls),
         },
     }
+    if all(CONFIGS.get(n, {}).get("entry") == "decode" for n in WORKLOADS[args.workload]):
+        # short-query launches read each KV head's keys once for a few rows: far below the ridge,
+        # bound by HBM. The launch time covers both kernels of the call (split and merge).
+        alg_bytes = sum(pc["bytes"] for pc in per_cfg) / len(calls)
+        gbs = alg_bytes / (kernel_ms_total / len(calls) * 1e-3) / 1e9
+        rec["roofline"] = {
+            "bound": "hbm",
+            "kernel": kernel_name(WORKLOADS[args.workload][0]),
+            "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "avg_launch_ms": round(kernel_ms_total / len(calls), 4),
+            "algorithmic_bytes_per_launch": alg_bytes,
+        }
     if not args.no_cpu_baseline:
         from oracle import host_workers
         workers = min(16, host_workers())

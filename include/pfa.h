@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define PFA_VERSION 10100 /* 1.1.0 */
+#define PFA_VERSION 10200 /* 1.2.0 */
 
 /* causal_offset < 0 selects bidirectional attention (no causal term). */
 #define PFA_NO_CAUSAL (-1)
@@ -57,18 +57,22 @@ extern "C" {
  * bit. */
 #define PFA_FLAG_NO_SKIP 1u
 
+/* Largest L accepted by the short-query (decode) entry point. */
+#define PFA_DECODE_MAX_L 64
+
 enum pfa_status {
   PFA_OK = 0,
-  PFA_ERR_NULL = 1,      /* Q, K, V, O (or a varlen prefix-sum buffer) is NULL                 */
+  PFA_ERR_NULL = 1,      /* Q, K, V, O, a varlen prefix-sum buffer or the decode workspace NULL */
   PFA_ERR_SIZE = 2,      /* a size < 1, L or S > PFA_MAX_LEN, or a size product / grid too big  */
   PFA_ERR_GQA = 3,       /* Hq is not a multiple of Hkv                                         */
   PFA_ERR_HEAD_DIM = 4,  /* D is not 64 or 128                                                  */
   PFA_ERR_MASK_ARGS = 5, /* window > 0 without the causal term                                  */
   PFA_ERR_SCALE = 6,     /* scale is not finite or not > 0                                      */
   PFA_ERR_ALIGN = 7,     /* Q, K, V or O not 16-byte aligned (prefix sums: not 4-byte aligned)  */
-  PFA_ERR_ALIAS = 8,     /* O overlaps Q, K, V, key_mask or a prefix-sum buffer                 */
+  PFA_ERR_ALIAS = 8,     /* O (or the decode workspace) overlaps another buffer of the call     */
   PFA_ERR_FLAGS = 9,     /* unknown bit in flags                                                */
-  PFA_ERR_LAUNCH = 10    /* the HIP launch failed (e.g. no gfx950 device is current)            */
+  PFA_ERR_LAUNCH = 10,   /* the HIP launch failed (e.g. no gfx950 device is current)            */
+  PFA_ERR_WORKSPACE = 11 /* decode workspace smaller than pfa_decode_workspace_bytes()          */
 };
 
 /*
@@ -145,6 +149,33 @@ int prefill_attn_gqa_varlen(const void* Q, const void* K, const void* V,
                             int n_seq, int max_seqlen_q, int total_q, int total_k,
                             int Hq, int Hkv, int D, float scale, int causal, int window,
                             void* O, void* stream);
+
+/*
+ * prefill_attn_gqa_decode -- the operation of prefill_attn_gqa for a short query chunk (one-token
+ * decode up to PFA_DECODE_MAX_L rows) against a long cache. tiny-llm Week 2 Day 5 Task 2 routes
+ * one-token decode and L <= 8 to a separate path; brotensor flash_attention_decode runs decode
+ * against a partially filled cache with query position valid_len - L_q + i, which is
+ * causal_offset = S - L here.
+ *
+ * Same arguments, layouts, masks and result as prefill_attn_gqa (1 <= L <= PFA_DECODE_MAX_L),
+ * plus a caller-owned DEVICE workspace of at least pfa_decode_workspace_bytes(B,Hq,Hkv,L,S,D)
+ * bytes, 16-byte aligned, not overlapping any other buffer of the call. The keys are split into
+ * ranges processed in parallel; each range leaves a partial (running max, sum, accumulator) per
+ * query row in the workspace, and a second kernel on the same stream merges the partials in a
+ * fixed order with the merge equations (tiny-llm Task 1), so the result is deterministic (run to
+ * run bit-identical) but not bit-identical to prefill_attn_gqa (another summation order). The
+ * workspace holds no state between calls; calls that share a workspace must be ordered (same
+ * stream). Returns a pfa_status code (PFA_ERR_WORKSPACE if the workspace is too small).
+ */
+int prefill_attn_gqa_decode(const void* Q, const void* K, const void* V,
+                            int B, int Hq, int Hkv, int L, int S, int D,
+                            float scale, int causal_offset, int window,
+                            const uint8_t* key_mask, void* O,
+                            void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes prefill_attn_gqa_decode needs for this shape (a pure function of the
+ * arguments), or -1 if the shape is invalid for it. */
+int64_t pfa_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* pfa_status_str(int status);

@@ -3,6 +3,7 @@
 The computation runs in ``libpfa.so`` (hand-written HIP); this package is its thin Python binding.
 """
 from ._binding import (  # noqa: F401
+    DECODE_MAX_L,
     EXPORTS,
     FLAG_NO_SKIP,
     LIB_PATH,
@@ -10,8 +11,11 @@ from ._binding import (  # noqa: F401
     NO_CAUSAL,
     STATUS,
     PfaError,
+    decode_workspace_bytes,
     library,
     prefill_attn_gqa,
+    prefill_attn_gqa_decode,
+    prefill_attn_gqa_decode_raw,
     prefill_attn_gqa_raw,
     prefill_attn_gqa_varlen,
     prefill_attn_gqa_varlen_raw,

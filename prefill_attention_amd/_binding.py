@@ -20,10 +20,11 @@ MAX_LEN = 1 << 30
 STATUS = {
     0: "PFA_OK", 1: "PFA_ERR_NULL", 2: "PFA_ERR_SIZE", 3: "PFA_ERR_GQA", 4: "PFA_ERR_HEAD_DIM",
     5: "PFA_ERR_MASK_ARGS", 6: "PFA_ERR_SCALE", 7: "PFA_ERR_ALIGN", 8: "PFA_ERR_ALIAS",
-    9: "PFA_ERR_FLAGS", 10: "PFA_ERR_LAUNCH",
+    9: "PFA_ERR_FLAGS", 10: "PFA_ERR_LAUNCH", 11: "PFA_ERR_WORKSPACE",
 }
-EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_varlen", "pfa_status_str",
-           "pfa_version")
+DECODE_MAX_L = 64
+EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_varlen", "prefill_attn_gqa_decode",
+           "pfa_decode_workspace_bytes", "pfa_status_str", "pfa_version")
 
 _lib = None
 
@@ -52,6 +53,10 @@ def library() -> ctypes.CDLL:
         lib.prefill_attn_gqa_varlen.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, ci,
                                                 vp, vp]
         lib.prefill_attn_gqa_varlen.restype = ci
+        lib.prefill_attn_gqa_decode.argtypes = sig[:-1] + [vp, ctypes.c_int64, vp]
+        lib.prefill_attn_gqa_decode.restype = ci
+        lib.pfa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
+        lib.pfa_decode_workspace_bytes.restype = ctypes.c_int64
         lib.pfa_status_str.argtypes = [ci]
         lib.pfa_status_str.restype = ctypes.c_char_p
         lib.pfa_version.argtypes = []
@@ -205,6 +210,80 @@ def prefill_attn_gqa_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: i
                                          cu_seqlens_k.data_ptr(), n_seq, int(max_seqlen_q), total_q, total_k,
                                          Hq, Hkv, D, float(scale), bool(causal), int(window), out.data_ptr(),
                                          stream_ptr)
+    if rc != 0:
+        raise PfaError(rc, status_str(rc))
+    return out
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, L: int, S: int, D: int) -> int:
+    """Bytes of workspace the decode entry point needs for this shape (-1 if invalid)."""
+    return int(library().pfa_decode_workspace_bytes(B, Hq, Hkv, L, S, D))
+
+
+def prefill_attn_gqa_decode_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: int, Hkv: int, L: int,
+                                S: int, D: int, scale: float, causal_offset: int, window: int,
+                                key_mask_ptr: int | None, o_ptr: int, ws_ptr: int | None, ws_bytes: int,
+                                stream: int | None) -> int:
+    """Direct C-ABI call of the short-query (decode) entry point; returns the status code."""
+    return int(library().prefill_attn_gqa_decode(
+        q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
+        key_mask_ptr or None, o_ptr, ws_ptr or None, ws_bytes, stream or None))
+
+
+def prefill_attn_gqa_decode(q, k, v, *, scale: float | None = None, causal: bool = True,
+                            causal_offset: int | None = None, window: int = 0, key_mask=None, out=None,
+                            workspace=None, stream=None):
+    """Short-query (decode, L <= 64) grouped-query attention on torch tensors: the same arguments
+    and result as prefill_attn_gqa, computed with the key range split over the chip and a
+    deterministic merge. `workspace` is an optional uint8 GPU tensor of at least
+    decode_workspace_bytes(...) bytes (allocated here if None; the library itself never allocates)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D bfloat16 GPU tensor")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+    B, Hq, L, D = q.shape
+    Bk, Hkv, S, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if causal:
+        if causal_offset is None:
+            causal_offset = S - L
+        if causal_offset < 0:
+            raise ValueError(f"causal attention needs causal_offset >= 0 (got {causal_offset})")
+    else:
+        if window > 0:
+            raise ValueError("a sliding window needs causal=True")
+        causal_offset = NO_CAUSAL
+    mask_ptr = None
+    if key_mask is not None:
+        if key_mask.dtype == torch.bool:
+            key_mask = key_mask.view(torch.uint8)
+        if key_mask.dtype != torch.uint8 or tuple(key_mask.shape) != (B, S) or key_mask.device != q.device \
+                or not key_mask.is_contiguous():
+            raise ValueError(f"key_mask must be a contiguous uint8 [B,S]=({B},{S}) tensor on {q.device}")
+        mask_ptr = key_mask.data_ptr()
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q on q's device")
+    need = decode_workspace_bytes(B, Hq, Hkv, L, S, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    stream_ptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        rc = prefill_attn_gqa_decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
+                                         float(scale), int(causal_offset), int(window), mask_ptr,
+                                         out.data_ptr(), workspace.data_ptr(), workspace.numel(), stream_ptr)
     if rc != 0:
         raise PfaError(rc, status_str(rc))
     return out

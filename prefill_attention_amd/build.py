@@ -22,7 +22,7 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-SOURCES = ["pfa_kernel.hip", "pfa_api.cpp"]
+SOURCES = ["pfa_kernel.hip", "pfa_decode.hip", "pfa_api.cpp"]
 
 
 def hipcc() -> str:

@@ -163,10 +163,96 @@ int prefill_attn_gqa_varlen(const void* Q, const void* K, const void* V,
   return pfa::launch_prefill(p);
 }
 
+}  // extern "C"
+
+namespace pfa {
+
+DecodePlan decode_plan(int B, int Hq, int Hkv, int L, int S, int D) {
+  // one round of single-wave workgroups (five fit a compute unit's LDS, 256 units), at least
+  // four 32-key tiles per split
+  constexpr long long kTargetGroups = 1280;
+  constexpr long long kMinTilesPerSplit = 4;
+  DecodePlan pl;
+  const long long R = static_cast<long long>(Hq / Hkv) * L;
+  pl.n_rowgrp = static_cast<int>((R + 63) / 64);
+  pl.rows_cap = static_cast<int>(R < 64 ? R : 64);
+  const long long tiles = (static_cast<long long>(S) + 31) / 32;
+  const long long units = static_cast<long long>(B) * Hkv * pl.n_rowgrp;
+  long long n_split = (kTargetGroups + units - 1) / units;
+  if (n_split > tiles) n_split = tiles;
+  if (n_split < 1) n_split = 1;
+  long long tps = (tiles + n_split - 1) / n_split;
+  if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
+  n_split = (tiles + tps - 1) / tps;
+  pl.n_split = static_cast<int>(n_split);
+  pl.tiles_per_split = static_cast<int>(tps);
+  pl.n_partials = units * n_split;
+  pl.workspace_bytes = pl.n_partials * pl.rows_cap * (static_cast<long long>(D) + 2) * 4;
+  return pl;
+}
+
+}  // namespace pfa
+
+extern "C" {
+
+int64_t pfa_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || S < 1 || Hq % Hkv != 0 || (D != 64 && D != 128) ||
+      L > PFA_DECODE_MAX_L || S > PFA_MAX_LEN || B > (1 << 20) || Hq > (1 << 20))
+    return -1;
+  return pfa::decode_plan(B, Hq, Hkv, L, S, D).workspace_bytes;
+}
+
+int prefill_attn_gqa_decode(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L,
+                            int S, int D, float scale, int causal_offset, int window,
+                            const uint8_t* key_mask, void* O, void* workspace, int64_t workspace_bytes,
+                            void* stream) {
+  int rc = validate(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window, key_mask, O, 0u);
+  if (rc != PFA_OK) return rc;
+  if (!workspace) return PFA_ERR_NULL;
+  if (L > PFA_DECODE_MAX_L || B > (1 << 20) || Hq > (1 << 20)) return PFA_ERR_SIZE;
+  const pfa::DecodePlan plan = pfa::decode_plan(B, Hq, Hkv, L, S, D);
+  if (plan.n_partials > INT_MAX || static_cast<long long>(B) * Hq * L > INT_MAX) return PFA_ERR_SIZE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 15u) return PFA_ERR_ALIGN;
+  if (workspace_bytes < plan.workspace_bytes) return PFA_ERR_WORKSPACE;
+  const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace);
+  const Range ws{w0, w0 + static_cast<uintptr_t>(plan.workspace_bytes)};
+  const auto bytes = [](long long a, long long b, long long c, long long d) {
+    return static_cast<uintptr_t>(a) * static_cast<uintptr_t>(b) * static_cast<uintptr_t>(c) *
+           static_cast<uintptr_t>(d) * 2u;
+  };
+  const auto at = [](const void* p, uintptr_t n) {
+    return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + n};
+  };
+  if (overlaps(ws, at(Q, bytes(B, Hq, L, D))) || overlaps(ws, at(K, bytes(B, Hkv, S, D))) ||
+      overlaps(ws, at(V, bytes(B, Hkv, S, D))) || overlaps(ws, at(O, bytes(B, Hq, L, D))) ||
+      (key_mask && overlaps(ws, at(key_mask, static_cast<uintptr_t>(B) * static_cast<uintptr_t>(S)))))
+    return PFA_ERR_ALIAS;
+  pfa::Launch p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.key_mask = key_mask;
+  p.o = O;
+  p.batch = B;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.group = Hq / Hkv;
+  p.lq = L;
+  p.sk = S;
+  p.d = D;
+  p.scale = scale;
+  p.causal = causal_offset >= 0 ? 1 : 0;
+  p.causal_offset = causal_offset < 0 ? PFA_NO_CAUSAL : causal_offset;
+  p.window = (causal_offset >= 0 && window > 0) ? window : 0;
+  p.flags = 0;
+  p.stream = stream;
+  return pfa::launch_decode(p, plan, workspace);
+}
+
 const char* pfa_status_str(int status) {
   switch (status) {
     case PFA_OK: return "ok";
-    case PFA_ERR_NULL: return "null pointer (Q, K, V, O and, for varlen, both prefix sums are required)";
+    case PFA_ERR_NULL: return "null pointer (Q, K, V, O and, for varlen, both prefix sums, for decode the workspace)";
     case PFA_ERR_SIZE: return "invalid size: B, Hq, Hkv, L, S, D must be >= 1 and fit the launch";
     case PFA_ERR_GQA: return "Hq must be a multiple of Hkv";
     case PFA_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
@@ -176,6 +262,7 @@ const char* pfa_status_str(int status) {
     case PFA_ERR_ALIAS: return "O must not overlap Q, K, V or key_mask";
     case PFA_ERR_FLAGS: return "unknown flag bit";
     case PFA_ERR_LAUNCH: return "HIP kernel launch failed (is a gfx950 device current?)";
+    case PFA_ERR_WORKSPACE: return "workspace smaller than pfa_decode_workspace_bytes() for this shape";
     default: return "unknown status";
   }
 }

@@ -1,0 +1,472 @@
+// Short-query (decode) attention for gfx950: L <= 64 query rows per head against a long cache,
+// with the key range split across workgroups and a deterministic merge.
+//
+// What is computed is exactly the operation of the prefill kernel (same masks and head map;
+// tiny-llm, Week 2 Day 5 "Tiled Dense Prefill Attention", Tasks 1 and 2). The pages send one-token
+// decode and L <= 8 to a separate path (tiny-llm Task 2) and run decode against a partially filled
+// cache (brotensor flash_attention_decode). Work here is bound by HBM bandwidth: each KV head's
+// keys are read once for all G * L query rows of its group (no per-head re-read), and the keys
+// are split into ranges processed by different single-wave workgroups so that the whole chip
+// streams the cache. Each range yields a partial (m, l, a) per row; a second kernel combines the
+// partials in a fixed order with the merge equations (tiny-llm Task 1: m' = max(m, m_b),
+// l' = e^(m - m') l + e^(m_b - m') l_b, a' likewise), so the result is deterministic.
+//
+// Decode-split kernel, one wave per workgroup:
+//  * rows: the G * L (query head, row) pairs of one KV head, packed 32 per MFMA block (up to 64
+//    per workgroup; more rows take more row groups);
+//  * keys: 32-key tiles of the split's range, fetched by buffer-load DMA into one of two LDS
+//    stages (the next tile lands while the current one is used);
+//  * scores transposed, S^T = K . Q^T (v_mfma_f32_32x32x16_bf16), so a lane owns one row;
+//    O^T = V^T . P^T with V^T read by ds_read_b64_tr_b16 and P from the score registers;
+//  * exact online softmax per tile in the base-2 domain (scores times scale * log2 e).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pfa.h"
+#include "pfa_internal.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int kTk = 32;  // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor dword 3: 32-bit format, per-byte bounds
+constexpr int kRowsPerGroup = 64;          // query rows of one workgroup (two 32-row MFMA blocks)
+
+template <int D>
+struct DGeo {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kTileBytes = kTk * kRowBytes;  // one K or V tile
+  static constexpr int kStageBytes = 2 * kTileBytes;  // K then V
+  static constexpr int kChunksPerRow = D / 8;
+  static constexpr int kRowsPerDma = 1024 / kRowBytes;
+  static constexpr int kDmaPerTile = kTileBytes / 1024;  // DMA instructions per matrix
+  static constexpr int KQ = D / 16;
+  static constexpr int DB = D / 32;
+  __device__ static int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+};
+
+struct DParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint8_t* key_mask;
+  float* ws;  // partials: [n_partials][rows_cap][D] accumulators, then [n_partials][rows_cap][2] (m, l)
+  int hq, hkv, group, lq, sk;
+  float c;
+  int causal, causal_offset, window;
+  int n_rowgrp, rows_cap, n_split, tiles_per_split;
+  long long n_partials;
+};
+
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// max(x, x of lane l^32) with one v_permlane32_swap_b32 (inline asm: the builtin returns its first
+// result for both outputs when given equal inputs; the nops cover the VALU -> permlane hazard)
+__device__ __forceinline__ float max_with_partner_half(float x) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return max2(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
+// N DMA instructions from a buffer of nrec bytes at base (wave-uniform) into LDS: instruction j
+// writes lane l's 16 bytes, read from byte offset off[j], to LDS address dst + 1024 j + 16 l.
+// Reads at or past nrec return zeros.
+template <int N>
+__device__ __forceinline__ void dma_rows(const void* base, int nrec, lds_char* dst, const unsigned* off) {
+  __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nrec, kBufferFlags);
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16,
+                                             off[j], 0, 0, 0);
+}
+
+template <int D, int RB, bool KMASK>
+__global__ __launch_bounds__(64) void pfa_decode_split_kernel(DParams p) {
+  using G = DGeo<D>;
+  constexpr int KQ = G::KQ;
+  constexpr int DB = G::DB;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * G::kStageBytes];
+
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // ---- workgroup -> (b, kv head, row group, split); splits of one (b, hk, rg) are adjacent ----
+  long long id = blockIdx.x;
+  const int split = (int)(id % p.n_split);
+  id /= p.n_split;
+  const int rg = (int)(id % p.n_rowgrp);
+  id /= p.n_rowgrp;
+  const int hk = (int)(id % p.hkv);
+  const int b = (int)(id / p.hkv);
+  const long long part = blockIdx.x;  // partial index (same numbering as the workgroups)
+  const int L = p.lq, S = p.sk;
+  const int R = p.group * L;  // rows of this KV head: (g, i) -> g * L + i
+
+  // ---- this lane's rows (one per MFMA block) and their visible key interval [lo, hi] ----
+  bf16x8 qreg[RB][KQ];
+  int row_lo[RB], row_hi[RB];
+  int grp_lo = S, grp_hi = -1;  // union over the workgroup's real rows (wave-uniform after reduction)
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = rg * kRowsPerGroup + rb * 32 + l32;
+    int lo = S, hi = -1;  // empty
+    if (r < R) {
+      const int g = r / L, i = r % L;
+      const uint16_t* qrow = p.q + (((long long)b * p.hq + hk * p.group + g) * L + i) * (long long)D;
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) qreg[rb][kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * hh);
+      lo = 0;
+      hi = S - 1;
+      if (p.causal) {
+        const long long pos = (long long)i + p.causal_offset;
+        hi = (int)(pos < hi ? pos : hi);
+        if (p.window > 0) {
+          const long long w0 = pos - p.window + 1;
+          lo = (int)(w0 > 0 ? w0 : 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) qreg[rb][kk][t] = (__bf16)0.0f;
+    }
+    row_lo[rb] = lo;
+    row_hi[rb] = hi;
+    if (lo <= hi) {
+      grp_lo = min(grp_lo, lo);
+      grp_hi = max(grp_hi, hi);
+    }
+  }
+  // wave-wide union of the rows' intervals
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    grp_lo = min(grp_lo, __shfl_xor(grp_lo, o));
+    grp_hi = max(grp_hi, __shfl_xor(grp_hi, o));
+  }
+
+  // ---- the split's tiles, clipped to the keys some row can see ----
+  const int n_tiles = (S + kTk - 1) / kTk;
+  int t_begin = split * p.tiles_per_split;
+  int t_end = min(t_begin + p.tiles_per_split, n_tiles);
+  if (grp_hi < grp_lo) {
+    t_end = t_begin;  // no row sees anything
+  } else {
+    t_begin = max(t_begin, grp_lo / kTk);
+    t_end = min(t_end, grp_hi / kTk + 1);
+  }
+  // visible iff tile key jj: lo <= key <= hi (and the key-mask byte is nonzero)
+  const uint16_t* kg = p.k + ((long long)b * p.hkv + hk) * (long long)S * D;
+  const uint16_t* vg = p.v + ((long long)b * p.hkv + hk) * (long long)S * D;
+  const uint8_t* mrow = KMASK ? p.key_mask + (long long)b * S : nullptr;
+
+  // DMA offsets (K and V rows of a tile; fixed per lane)
+  unsigned off_k[G::kDmaPerTile], off_v[G::kDmaPerTile];
+#pragma unroll
+  for (int j = 0; j < G::kDmaPerTile; ++j) {
+    const int row = j * G::kRowsPerDma + lane / G::kChunksPerRow;
+    const int pch = lane % G::kChunksPerRow;
+    off_k[j] = (unsigned)(row * G::kRowBytes + 16 * (pch ^ G::swz_k(row)));
+    off_v[j] = (unsigned)(row * G::kRowBytes + 16 * (pch ^ G::swz_v(row)));
+  }
+  auto uniform_ptr = [&](const void* ptr) __attribute__((always_inline)) -> const void* {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(ptr);
+    // readfirstlane returns int: go through unsigned so the low word is not sign-extended
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32));
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a);
+    return reinterpret_cast<const void*>(((uintptr_t)hi << 32) | (uintptr_t)lo);
+  };
+  auto issue = [&](int t, char* stage) __attribute__((always_inline)) {
+    const long long key0 = (long long)t * kTk;
+    const long long rows = (long long)S - key0;
+    const int nrec = __builtin_amdgcn_readfirstlane((rows < kTk ? (int)rows : kTk) * G::kRowBytes);
+    dma_rows<G::kDmaPerTile>(uniform_ptr(kg + key0 * D), nrec, (lds_char*)stage, off_k);
+    dma_rows<G::kDmaPerTile>(uniform_ptr(vg + key0 * D), nrec, (lds_char*)stage + G::kTileBytes, off_v);
+  };
+
+  // LDS read addresses inside a stage (as in the prefill kernel, with one 32-key block)
+  int a_k, a_v;
+  {
+    const int x = G::swz_k(l32);
+    a_k = l32 * G::kRowBytes + 16 * (hh ^ (x & 1)) + 32 * (x >> 1);
+    const int g16 = lane >> 4, loc = lane & 15, r4 = loc >> 2, cc = loc & 3;
+    const int row = 4 * (g16 >> 1) + r4;
+    a_v = G::kTileBytes + row * G::kRowBytes + 64 * (G::swz_v(row) >> 2) + 32 * (g16 & 1) + 8 * cc;
+  }
+
+  f32x16 acc[RB][DB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][db][v] = 0.0f;
+  float m[RB], l[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.0f;
+  }
+  const float c = p.c;
+
+  if (t_begin < t_end) issue(t_begin, lds_raw);
+  // One step: tile t is in `cur`, tile t+1 is fetched into `nxt`. The stages are restrict
+  // pointers: the fetch into `nxt` is never read in the step, which lets the compiler keep it in
+  // flight across the step's LDS reads (it is waited for at the top of the next step).
+  auto step = [&](int t, char* __restrict__ cur, char* __restrict__ nxt) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t has landed (one wave: no barrier)
+    // the other stage's reads (previous tile) all completed before their MFMAs; refill it
+    if (t + 1 < t_end) issue(t + 1, nxt);
+    const lds_char* base = (const lds_char*)cur;
+    // scores
+    f32x16 s[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[rb][v] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) {
+      const bf16x8 a = *(const lds_bf16x8*)(base + (a_k ^ (32 * kk)));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[rb][kk], s[rb], 0, 0, 0);
+    }
+    // mask: lane row's interval and the key bytes
+    const int key0 = t * kTk;
+    uint32_t mb[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    if (KMASK) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = key0 + 8 * j + 4 * hh + i;
+          const uint32_t byte = key < S ? (uint32_t)mrow[key] : 0u;
+          w |= (byte != 0u ? 0xFFu : 0u) << (8 * i);
+        }
+        mb[j] = w;
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      // key visible iff 0 <= key - lo <= span (one unsigned compare); an empty row gets lo past
+      // every key (key - lo < 0, a huge unsigned value) and span 0
+      const bool empty = row_hi[rb] < row_lo[rb];
+      const unsigned span = empty ? 0u : (unsigned)(row_hi[rb] - row_lo[rb]);
+      const int lo = empty ? S + kTk : row_lo[rb];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = key0 + 8 * j + 4 * hh + i;
+          const bool vis = ((unsigned)(key - lo) <= span) & (((mb[j] >> (8 * i)) & 0xFFu) != 0u);
+          s[rb][4 * j + i] = vis ? s[rb][4 * j + i] : -INFINITY;
+        }
+    }
+    // exact online softmax per row, P in bf16 pairs, row sums of the rounded P
+    unsigned pw[RB][8];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float mx = s[rb][0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = max2(mx, s[rb][v]);
+      mx = max_with_partner_half(mx) * c;
+      const float mnew = max2(m[rb], mx);
+      const float msub = (mnew == -INFINITY) ? 0.0f : mnew;
+      const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m[rb] - mnew);
+      float ls[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][2 * w], c, -msub));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][2 * w + 1], c, -msub));
+        const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+        ls[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, ls[w & 1], false);
+        pw[rb][w] = __builtin_bit_cast(unsigned, pr);
+      }
+      l[rb] = l[rb] * alpha + (ls[0] + ls[1]);
+      m[rb] = mnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[rb][db][v] *= alpha;
+    }
+    // O^T += V^T . P^T over the tile's two 16-key steps
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const lds_char* pr = base + 16 * c2 * G::kRowBytes + (a_v ^ (64 * db));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pr);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pr + 8 * G::kRowBytes));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const u32x4 w = {pw[rb][4 * c2], pw[rb][4 * c2 + 1], pw[rb][4 * c2 + 2], pw[rb][4 * c2 + 3]};
+          acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, w), acc[rb][db], 0, 0, 0);
+        }
+      }
+  };
+  for (int t = t_begin; t < t_end; ++t) {
+    if (((t - t_begin) & 1) == 0)
+      step(t, lds_raw, lds_raw + G::kStageBytes);
+    else
+      step(t, lds_raw + G::kStageBytes, lds_raw);
+  }
+
+  // ---- the partial of this workgroup: acc (unnormalised), m (base-2 domain), l ----
+  const int rows_cap = p.rows_cap;
+  float* ws_acc = p.ws + (size_t)part * rows_cap * D;
+  float* ws_ml = p.ws + (size_t)p.n_partials * rows_cap * D + (size_t)part * rows_cap * 2;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rr = rb * 32 + l32;  // row within the group
+    const float lt = l[rb] + __shfl_xor(l[rb], 32);
+    if (rr < rows_cap) {
+      float* dst = ws_acc + (size_t)rr * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 o4 = {acc[rb][db][4 * j], acc[rb][db][4 * j + 1], acc[rb][db][4 * j + 2], acc[rb][db][4 * j + 3]};
+          *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * j + 4 * hh) = o4;
+        }
+      if (hh == 0) {
+        ws_ml[2 * rr] = m[rb];
+        ws_ml[2 * rr + 1] = lt;
+      }
+    }
+  }
+}
+
+// One workgroup per output row (b, h, i): combine the row's n_split partials with the merge
+// equations and write O = a / l in BF16 (0 when no key was visible). Thread t owns four columns
+// (d4 = t % (D/4)) of the splits s = j, j + P, ... (j = t / (D/4), P = kMergeThreads / (D/4)), so
+// every thread has several independent loads in flight; the P partial sums are then added by a
+// fixed tree over j, so the result does not depend on timing.
+constexpr int kMergeThreads = 1024;
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void pfa_decode_merge_kernel(DParams p, uint16_t* o) {
+  constexpr int C4 = D / 4;              // float4 columns
+  constexpr int P = kMergeThreads / C4;  // split lanes
+  __shared__ f32x4 red[kMergeThreads];
+  __shared__ float red_m[kMergeThreads];
+  __shared__ float red_l[P];
+  const int t = threadIdx.x;
+  const int d4 = t % C4, j = t / C4;
+  long long id = blockIdx.x;  // (b, h, i)
+  const int i = (int)(id % p.lq);
+  id /= p.lq;
+  const int h = (int)(id % p.hq);
+  const int b = (int)(id / p.hq);
+  const int hk = h / p.group, g = h % p.group;
+  const int r = g * p.lq + i;
+  const int rg = r / kRowsPerGroup, rr = r % kRowsPerGroup;
+  const long long part0 = (((long long)b * p.hkv + hk) * p.n_rowgrp + rg) * p.n_split;
+  const float* ws_ml = p.ws + (size_t)p.n_partials * p.rows_cap * D;
+  // m* = max over the splits
+  float mloc = -INFINITY;
+  for (int s = t; s < p.n_split; s += kMergeThreads) mloc = max2(mloc, ws_ml[(size_t)(part0 + s) * p.rows_cap * 2 + 2 * rr]);
+  red_m[t] = mloc;
+  __syncthreads();
+  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
+    if (t < w) red_m[t] = max2(red_m[t], red_m[t + w]);
+    __syncthreads();
+  }
+  const float mstar = red_m[0];
+  float lsum = 0.0f;
+  f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (mstar != -INFINITY) {
+#pragma unroll 4
+    for (int s = j; s < p.n_split; s += P) {
+      const size_t q = (size_t)(part0 + s);
+      const float w = __builtin_amdgcn_exp2f(ws_ml[q * p.rows_cap * 2 + 2 * rr] - mstar);  // 0 for empty splits
+      lsum = __builtin_fmaf(w, ws_ml[q * p.rows_cap * 2 + 2 * rr + 1], lsum);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p.ws + (q * p.rows_cap + rr) * D + 4 * d4);
+      a += w * v;
+    }
+  }
+  red[t] = a;
+  if (d4 == 0) red_l[j] = lsum;
+  __syncthreads();
+  // fixed tree over the split lanes j (red[j * C4 + d4])
+  for (int w = P / 2; w > 0; w >>= 1) {
+    if (j < w) {
+      red[t] += red[t + w * C4];
+      if (d4 == 0) red_l[j] += red_l[j + w];
+    }
+    __syncthreads();
+  }
+  if (j == 0) {
+    const float lt = red_l[0];
+    const f32x4 at = red[d4];
+    uint16_t* orow = o + (((long long)b * p.hq + h) * p.lq + i) * D + 4 * d4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float out = lt > 0.0f ? at[k] / lt : 0.0f;
+      const __bf16 ob = (__bf16)out;
+      orow[k] = __builtin_bit_cast(uint16_t, ob);
+    }
+  }
+}
+
+template <int D, int RB>
+int launch_decode_variant(const pfa::Launch& L, const pfa::DecodePlan& plan, void* ws) {
+  DParams p;
+  p.q = static_cast<const uint16_t*>(L.q);
+  p.k = static_cast<const uint16_t*>(L.k);
+  p.v = static_cast<const uint16_t*>(L.v);
+  p.key_mask = L.key_mask;
+  p.ws = static_cast<float*>(ws);
+  p.hq = L.hq;
+  p.hkv = L.hkv;
+  p.group = L.group;
+  p.lq = L.lq;
+  p.sk = L.sk;
+  p.c = L.scale * kLog2e;
+  p.causal = L.causal;
+  p.causal_offset = L.causal_offset;
+  p.window = L.window;
+  p.n_rowgrp = plan.n_rowgrp;
+  p.rows_cap = plan.rows_cap;
+  p.n_split = plan.n_split;
+  p.tiles_per_split = plan.tiles_per_split;
+  p.n_partials = plan.n_partials;
+  hipStream_t stream = static_cast<hipStream_t>(L.stream);
+  void* args[] = {&p};
+  const void* fn = L.key_mask ? reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, true>)
+                              : reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, false>);
+  if (hipLaunchKernel(fn, dim3((unsigned)plan.n_partials), dim3(64), args, 0, stream) != hipSuccess)
+    return PFA_ERR_LAUNCH;
+  uint16_t* o = static_cast<uint16_t*>(L.o);
+  void* margs[] = {&p, &o};
+  const long long rows = (long long)L.batch * L.hq * L.lq;
+  if (hipLaunchKernel(reinterpret_cast<const void*>(&pfa_decode_merge_kernel<D>), dim3((unsigned)rows),
+                      dim3(kMergeThreads), margs, 0, stream) != hipSuccess)
+    return PFA_ERR_LAUNCH;
+  return PFA_OK;
+}
+
+}  // namespace
+
+namespace pfa {
+
+int launch_decode(const Launch& p, const DecodePlan& plan, void* workspace) {
+  const bool two = plan.rows_cap > 32;
+  if (p.d == 128) return two ? launch_decode_variant<128, 2>(p, plan, workspace) : launch_decode_variant<128, 1>(p, plan, workspace);
+  return two ? launch_decode_variant<64, 2>(p, plan, workspace) : launch_decode_variant<64, 1>(p, plan, workspace);
+}
+
+}  // namespace pfa

@@ -37,4 +37,21 @@ long long grid_blocks(const Launch& p);
 // Enqueue the prefill kernel. Returns PFA_OK or PFA_ERR_LAUNCH.
 int launch_prefill(const Launch& p);
 
+// Work split of the short-query (decode) path, a pure function of the shape so that the
+// workspace query and the launch agree: the rows of one KV head (G * L) in row groups of up to 64,
+// the keys in n_split ranges of tiles_per_split 32-key tiles, one partial per
+// (b, kv head, row group, split).
+struct DecodePlan {
+  int n_rowgrp = 0;
+  int rows_cap = 0;  // rows stored per partial: min(G * L, 64)
+  int n_split = 0;
+  int tiles_per_split = 0;
+  long long n_partials = 0;
+  long long workspace_bytes = 0;
+};
+DecodePlan decode_plan(int B, int Hq, int Hkv, int L, int S, int D);
+
+// Enqueue the split kernel and the merge kernel. Returns PFA_OK or PFA_ERR_LAUNCH.
+int launch_decode(const Launch& p, const DecodePlan& plan, void* workspace);
+
 }  // namespace pfa

@@ -178,3 +178,48 @@ def test_varlen_binding_rejects_bad_tensors():
     cu = torch.tensor([0, 10], dtype=torch.int32)
     with pytest.raises(ValueError, match="3-D bfloat16 GPU"):
         pfa.prefill_attn_gqa_varlen(q, k, k, cu, cu, 10)
+
+
+# ---- short-query (decode) entry point ----
+WS = 8 * A
+DGOOD = dict(GOOD, L=4, S=1000, off=996, ws=WS, wsb=None)
+
+
+def dcall(**kw):
+    a = dict(DGOOD)
+    a.update(kw)
+    need = pfa.decode_workspace_bytes(a["B"], a["Hq"], a["Hkv"], a["L"], a["S"], a["D"])
+    wsb = need if a["wsb"] is None else a["wsb"]
+    return pfa.prefill_attn_gqa_decode_raw(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["L"], a["S"],
+                                           a["D"], a["scale"], a["off"], a["window"], a["mask"], a["o"], a["ws"],
+                                           wsb, a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(o=0), 1), (dict(ws=0), 1),
+    (dict(L=0), 2), (dict(S=0), 2), (dict(L=65), 2), (dict(B=2 ** 21), 2),
+    (dict(Hq=6, Hkv=4), 3), (dict(D=96), 4), (dict(off=-1, window=5), 5), (dict(scale=0.0), 6),
+    (dict(ws=WS + 8), 7), (dict(q=Q + 2), 7),
+    (dict(wsb=0), 11), (dict(wsb=-1), 11),
+    (dict(ws=Q), 8), (dict(ws=O - 16), 8), (dict(ws=K + 64), 8),
+], ids=lambda x: str(x))
+def test_decode_invalid_arguments_rejected(lib, kw, code):
+    assert dcall(**kw) == code
+
+
+def test_decode_workspace_too_small_by_one_byte(lib):
+    need = pfa.decode_workspace_bytes(1, 4, 2, 4, 1000, 128)
+    assert need > 0 and need % 16 == 0
+    assert dcall(wsb=need - 1) == 11
+
+
+def test_decode_workspace_bytes_function(lib):
+    defines, _ = header_defines()
+    assert defines["PFA_DECODE_MAX_L"] == pfa.DECODE_MAX_L
+    assert pfa.decode_workspace_bytes(1, 32, 8, 1, 32768, 128) > 0
+    for bad in [(0, 32, 8, 1, 100, 128), (1, 32, 8, 0, 100, 128), (1, 32, 8, 65, 100, 128), (1, 30, 8, 1, 100, 128),
+                (1, 32, 8, 1, 100, 96), (1, 32, 8, 1, 0, 128)]:
+        assert pfa.decode_workspace_bytes(*bad) == -1, bad
+    # a pure function of the shape, growing with the rows kept per partial
+    assert pfa.decode_workspace_bytes(1, 32, 8, 4, 4096, 128) == pfa.decode_workspace_bytes(1, 32, 8, 4, 4096, 128)
+    assert pfa.decode_workspace_bytes(1, 32, 8, 8, 4096, 128) > pfa.decode_workspace_bytes(1, 32, 8, 1, 4096, 128)

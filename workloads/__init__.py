@@ -44,6 +44,14 @@ CONFIGS: dict[str, dict] = {
     # Batched bidirectional prefill with per-sequence key padding (encoder-style prefill).
     "bidir_padded_b8": dict(B=8, Hq=32, Hkv=8, D=128, L=4096, S=4096, causal_offset=NO_CAUSAL,
                             window=0, amp=1.0, key_padding=(1024, 4096)),
+    # Short-query chunks for the decode entry point (tiny-llm Task 2 routes one-token decode and
+    # L <= 8 to a separate path; brotensor flash_attention_decode: query position valid_len - L + i).
+    "decode_l1_32k": dict(B=1, Hq=32, Hkv=8, D=128, L=1, S=32768, causal_offset=32767, window=0,
+                          amp=1.0, key_padding=None, entry="decode"),
+    "decode_l8_8k": dict(B=1, Hq=56, Hkv=8, D=128, L=8, S=8192, causal_offset=8184, window=0,
+                         amp=1.0, key_padding=None, entry="decode"),
+    "decode_b8_l1_4k": dict(B=8, Hq=32, Hkv=8, D=128, L=1, S=4096, causal_offset=4095, window=0,
+                            amp=1.0, key_padding=None, entry="decode"),
 }
 
 
