@@ -43,6 +43,7 @@ WORKLOADS = {
     "small_prompt_128": ["small_prompt_128"],
     "causal_witness_33x47": ["causal_witness_33x47"],
     "varlen_causal_b8": ["varlen_causal_b8"],
+    "ring_w1024_l2048": ["ring_w1024_l2048"],
     "decode_l1_32k": ["decode_l1_32k"],
     "decode_l8_8k": ["decode_l8_8k"],
     "decode_b8_l1_4k": ["decode_b8_l1_4k"],
@@ -169,12 +170,14 @@ def kernel_name(workload_name: str) -> str:
     from workloads import CONFIGS, VARLEN_CONFIGS
 
     if workload_name in VARLEN_CONFIGS:
-        return "pfa_prefill_kernel<%d,false>" % VARLEN_CONFIGS[workload_name]["D"]
+        return "pfa_prefill_kernel<%d,false,false>" % VARLEN_CONFIGS[workload_name]["D"]
     c = CONFIGS[workload_name]
+    if c.get("entry") == "ring":
+        return "pfa_prefill_kernel<%d,false,true> (after pfa_ring_append_kernel)" % c["D"]
     if c.get("entry") == "decode":
         return "pfa_decode_split_kernel<%d,%d,%s> + pfa_decode_merge_kernel<%d>" % (
             c["D"], 2 if (c["Hq"] // c["Hkv"]) * c["L"] > 32 else 1, "true" if c["key_padding"] else "false", c["D"])
-    return "pfa_prefill_kernel<%d,%s>" % (c["D"], "true" if c["key_padding"] else "false")
+    return "pfa_prefill_kernel<%d,%s,false>" % (c["D"], "true" if c["key_padding"] else "false")
 
 
 def varlen_cpu_baseline(name: str, workers: int, budget_s: float = 20.0) -> dict:
@@ -287,6 +290,19 @@ def main() -> int:
 
         def launch(q=q, k=k, v=v, kw=kw, fn=fn):
             fn(q, k, v, **kw)
+
+        if c.get("entry") == "ring":
+            pos0, ring = c["causal_offset"], c["ring"]
+            k_new, v_new = k[:, :, pos0:].contiguous(), v[:, :, pos0:].contiguous()
+            k_ring = torch.zeros(c["B"], c["Hkv"], ring, c["D"], dtype=torch.bfloat16, device=dev)
+            v_ring = torch.zeros_like(k_ring)
+            for p0 in range(max(0, pos0 - ring), pos0):
+                k_ring[:, :, p0 % ring] = k[:, :, p0]
+                v_ring[:, :, p0 % ring] = v[:, :, p0]
+
+            def launch(q=q, k_new=k_new, v_new=v_new, k_ring=k_ring, v_ring=v_ring, pos0=pos0, c=c, out=out):
+                pfa.prefill_attn_gqa_ring(q, k_new, v_new, k_ring, v_ring, pos0, scale=float(x["scale"]),
+                                          window=c["window"], out=out)
 
         calls.append((name, launch))
         per_cfg.append(dict(name=name, flops=flops, rows=c["B"] * c["L"], bytes=algorithmic_bytes(c)))

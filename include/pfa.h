@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define PFA_VERSION 10200 /* 1.2.0 */
+#define PFA_VERSION 10300 /* 1.3.0 */
 
 /* causal_offset < 0 selects bidirectional attention (no causal term). */
 #define PFA_NO_CAUSAL (-1)
@@ -72,7 +72,8 @@ enum pfa_status {
   PFA_ERR_ALIAS = 8,     /* O (or the decode workspace) overlaps another buffer of the call     */
   PFA_ERR_FLAGS = 9,     /* unknown bit in flags                                                */
   PFA_ERR_LAUNCH = 10,   /* the HIP launch failed (e.g. no gfx950 device is current)            */
-  PFA_ERR_WORKSPACE = 11 /* decode workspace smaller than pfa_decode_workspace_bytes()          */
+  PFA_ERR_WORKSPACE = 11, /* decode workspace smaller than pfa_decode_workspace_bytes()         */
+  PFA_ERR_RING = 12       /* ring cache smaller than 64 slots or than the keys the chunk sees   */
 };
 
 /*
@@ -149,6 +150,38 @@ int prefill_attn_gqa_varlen(const void* Q, const void* K, const void* V,
                             int n_seq, int max_seqlen_q, int total_q, int total_k,
                             int Hq, int Hkv, int D, float scale, int causal, int window,
                             void* O, void* stream);
+
+/*
+ * prefill_attn_gqa_ring -- causal (optionally sliding-window) prefill of a chunk against a rotating
+ * KV cache, with the chunk's own keys appended to the cache by the same call.
+ *
+ * TensorFold PR "Spark2.5's and Llama's prompt attention from one source", "What changes": the
+ * sliding layer reads each key and value row from its ring slot (RING = WINDOW + 64 there); the
+ * brotensor kv_cache_append comment: the new rows are copied into the cache at the current length.
+ *
+ *   Q             bf16 [B, Hq, L, D]    the chunk's queries, at positions pos0 .. pos0 + L - 1
+ *   K_new, V_new  bf16 [B, Hkv, L, D]   the chunk's keys / values (positions pos0 .. pos0 + L - 1)
+ *   K_ring, V_ring bf16 [B, Hkv, ring, D]  the rotating cache: key position j lives in slot
+ *                 j mod ring. On entry it must hold every position the chunk's rows see before
+ *                 pos0; on return the chunk's rows have been written to their slots (the cache
+ *                 then holds positions up to pos0 + L - 1). Written by the call.
+ *   pos0          position of the chunk's first row (>= 0)
+ *   ring          slots of the cache; >= 64 and >= min(window - 1 + L, pos0 + L) (with a window)
+ *                 or >= pos0 + L (without one), so that appending the chunk overwrites no key a
+ *                 row still sees
+ *   window        > 0: row at position p sees keys [max(0, p - window + 1), p]; <= 0: all of [0, p]
+ *   O             bf16 [B, Hq, L, D], fully overwritten
+ *
+ * The append runs first and the attention then reads every key through the slot map (no gather
+ * copy); both are enqueued on `stream` in that order. The result is bit-identical to
+ * prefill_attn_gqa on the logical keys (history followed by K_new) with causal_offset = pos0.
+ * Returns a pfa_status code (PFA_ERR_RING if the ring is too small; on error nothing is enqueued
+ * and neither O nor the cache is touched).
+ */
+int prefill_attn_gqa_ring(const void* Q, const void* K_new, const void* V_new,
+                          void* K_ring, void* V_ring,
+                          int B, int Hq, int Hkv, int L, int pos0, int ring, int D,
+                          float scale, int window, void* O, void* stream);
 
 /*
  * prefill_attn_gqa_decode -- the operation of prefill_attn_gqa for a short query chunk (one-token

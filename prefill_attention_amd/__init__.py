@@ -17,6 +17,8 @@ from ._binding import (  # noqa: F401
     prefill_attn_gqa_decode,
     prefill_attn_gqa_decode_raw,
     prefill_attn_gqa_raw,
+    prefill_attn_gqa_ring,
+    prefill_attn_gqa_ring_raw,
     prefill_attn_gqa_varlen,
     prefill_attn_gqa_varlen_raw,
     status_str,

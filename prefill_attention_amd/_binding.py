@@ -20,11 +20,11 @@ MAX_LEN = 1 << 30
 STATUS = {
     0: "PFA_OK", 1: "PFA_ERR_NULL", 2: "PFA_ERR_SIZE", 3: "PFA_ERR_GQA", 4: "PFA_ERR_HEAD_DIM",
     5: "PFA_ERR_MASK_ARGS", 6: "PFA_ERR_SCALE", 7: "PFA_ERR_ALIGN", 8: "PFA_ERR_ALIAS",
-    9: "PFA_ERR_FLAGS", 10: "PFA_ERR_LAUNCH", 11: "PFA_ERR_WORKSPACE",
+    9: "PFA_ERR_FLAGS", 10: "PFA_ERR_LAUNCH", 11: "PFA_ERR_WORKSPACE", 12: "PFA_ERR_RING",
 }
 DECODE_MAX_L = 64
-EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_varlen", "prefill_attn_gqa_decode",
-           "pfa_decode_workspace_bytes", "pfa_status_str", "pfa_version")
+EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_varlen", "prefill_attn_gqa_ring",
+           "prefill_attn_gqa_decode", "pfa_decode_workspace_bytes", "pfa_status_str", "pfa_version")
 
 _lib = None
 
@@ -57,6 +57,8 @@ def library() -> ctypes.CDLL:
         lib.prefill_attn_gqa_decode.restype = ci
         lib.pfa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
         lib.pfa_decode_workspace_bytes.restype = ctypes.c_int64
+        lib.prefill_attn_gqa_ring.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp, vp]
+        lib.prefill_attn_gqa_ring.restype = ci
         lib.pfa_status_str.argtypes = [ci]
         lib.pfa_status_str.restype = ctypes.c_char_p
         lib.pfa_version.argtypes = []
@@ -284,6 +286,52 @@ def prefill_attn_gqa_decode(q, k, v, *, scale: float | None = None, causal: bool
         rc = prefill_attn_gqa_decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
                                          float(scale), int(causal_offset), int(window), mask_ptr,
                                          out.data_ptr(), workspace.data_ptr(), workspace.numel(), stream_ptr)
+    if rc != 0:
+        raise PfaError(rc, status_str(rc))
+    return out
+
+
+def prefill_attn_gqa_ring_raw(q_ptr: int, kn_ptr: int, vn_ptr: int, kr_ptr: int, vr_ptr: int, B: int, Hq: int,
+                              Hkv: int, L: int, pos0: int, ring: int, D: int, scale: float, window: int,
+                              o_ptr: int, stream: int | None) -> int:
+    """Direct C-ABI call of the rotating-cache entry point; returns the status code."""
+    return int(library().prefill_attn_gqa_ring(q_ptr, kn_ptr, vn_ptr, kr_ptr, vr_ptr, B, Hq, Hkv, L, pos0, ring, D,
+                                               ctypes.c_float(scale), window, o_ptr, stream or None))
+
+
+def prefill_attn_gqa_ring(q, k_new, v_new, k_ring, v_ring, pos0: int, *, scale: float | None = None,
+                          window: int = 0, out=None, stream=None):
+    """Causal (optionally windowed) prefill of a chunk at positions pos0.. against a rotating cache,
+    appending the chunk's keys first. q: bf16 [B,Hq,L,D]; k_new, v_new: bf16 [B,Hkv,L,D]; k_ring,
+    v_ring: bf16 [B,Hkv,ring,D] (position j in slot j % ring; updated in place). Returns `out`."""
+    import torch
+
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_ring", k_ring), ("v_ring", v_ring)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 4 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous 4-D bfloat16 tensor on {q.device}")
+    B, Hq, L, D = q.shape
+    Bn, Hkv, Ln, Dn = k_new.shape
+    if tuple(v_new.shape) != tuple(k_new.shape) or (Bn, Ln, Dn) != (B, L, D):
+        raise ValueError(f"k_new / v_new must be [B,Hkv,L,D]: q {tuple(q.shape)}, k_new {tuple(k_new.shape)}")
+    ring = k_ring.shape[2]
+    if tuple(k_ring.shape) != (B, Hkv, ring, D) or tuple(v_ring.shape) != tuple(k_ring.shape):
+        raise ValueError(f"k_ring / v_ring must be [B,Hkv,ring,D]: {tuple(k_ring.shape)}, {tuple(v_ring.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    stream_ptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        rc = prefill_attn_gqa_ring_raw(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_ring.data_ptr(),
+                                       v_ring.data_ptr(), B, Hq, Hkv, L, int(pos0), ring, D, float(scale),
+                                       int(window), out.data_ptr(), stream_ptr)
     if rc != 0:
         raise PfaError(rc, status_str(rc))
     return out

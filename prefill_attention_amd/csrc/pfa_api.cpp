@@ -1,5 +1,6 @@
 // C-ABI entry points: argument validation (host only, before anything is enqueued) and dispatch
 // to the HIP launcher. This file uses no HIP API, so its checks run without a GPU.
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -195,6 +196,66 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int L, int S, int D) {
 
 extern "C" {
 
+int prefill_attn_gqa_ring(const void* Q, const void* K_new, const void* V_new, void* K_ring, void* V_ring, int B,
+                          int Hq, int Hkv, int L, int pos0, int ring, int D, float scale, int window, void* O,
+                          void* stream) {
+  if (!Q || !K_new || !V_new || !K_ring || !V_ring || !O) return PFA_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1 || pos0 < 0 || ring < 1) return PFA_ERR_SIZE;
+  if (static_cast<long long>(pos0) + L > PFA_MAX_LEN || ring > PFA_MAX_LEN) return PFA_ERR_SIZE;
+  const long long lim = LLONG_MAX / 4;
+  long long q_elems, new_elems, ring_elems, t;
+  if (!mul_fits(B, Hq, lim, &t) || !mul_fits(t, L, lim, &t) || !mul_fits(t, D, lim, &q_elems)) return PFA_ERR_SIZE;
+  if (!mul_fits(B, Hkv, lim, &t) || !mul_fits(t, L, lim, &t) || !mul_fits(t, D, lim, &new_elems)) return PFA_ERR_SIZE;
+  if (!mul_fits(B, Hkv, lim, &t) || !mul_fits(t, ring, lim, &t) || !mul_fits(t, D, lim, &ring_elems))
+    return PFA_ERR_SIZE;
+  if (Hq % Hkv != 0) return PFA_ERR_GQA;
+  if (D != 64 && D != 128) return PFA_ERR_HEAD_DIM;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return PFA_ERR_SCALE;
+  // the ring must hold every key some row of the chunk sees, after the chunk is appended
+  const long long all = static_cast<long long>(pos0) + L;
+  const long long need = window > 0 ? std::min(static_cast<long long>(window) - 1 + L, all) : all;
+  if (ring < 64 || ring < need) return PFA_ERR_RING;
+  const uintptr_t a16 = 15;
+  for (const void* ptr : {Q, static_cast<const void*>(K_new), static_cast<const void*>(V_new),
+                          static_cast<const void*>(K_ring), static_cast<const void*>(V_ring),
+                          static_cast<const void*>(O)})
+    if (reinterpret_cast<uintptr_t>(ptr) & a16) return PFA_ERR_ALIGN;
+  const auto at = [](const void* p, long long elems) {
+    return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + static_cast<uintptr_t>(elems) * 2u};
+  };
+  const Range ro = at(O, q_elems), rq = at(Q, q_elems), rkn = at(K_new, new_elems), rvn = at(V_new, new_elems);
+  const Range rkr = at(K_ring, ring_elems), rvr = at(V_ring, ring_elems);
+  // O and the two rings are written; none may overlap another buffer of the call
+  if (overlaps(ro, rq) || overlaps(ro, rkn) || overlaps(ro, rvn) || overlaps(ro, rkr) || overlaps(ro, rvr) ||
+      overlaps(rkr, rq) || overlaps(rkr, rkn) || overlaps(rkr, rvn) || overlaps(rkr, rvr) ||
+      overlaps(rvr, rq) || overlaps(rvr, rkn) || overlaps(rvr, rvn))
+    return PFA_ERR_ALIAS;
+  int rc = pfa::launch_ring_append(K_new, V_new, K_ring, V_ring, B, Hkv, L, D, ring, pos0, stream);
+  if (rc != PFA_OK) return rc;
+  pfa::Launch p;
+  p.q = Q;
+  p.k = K_ring;
+  p.v = V_ring;
+  p.key_mask = nullptr;
+  p.o = O;
+  p.batch = B;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.group = Hq / Hkv;
+  p.lq = L;
+  p.sk = pos0 + L;  // positions 0 .. pos0 + L - 1, read through the ring
+  p.d = D;
+  p.scale = scale;
+  p.causal = 1;
+  p.causal_offset = pos0;
+  p.window = window > 0 ? window : 0;
+  p.flags = 0;
+  p.stream = stream;
+  p.ring = ring;
+  if (pfa::grid_blocks(p) > INT_MAX) return PFA_ERR_SIZE;
+  return pfa::launch_prefill(p);
+}
+
 int64_t pfa_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D) {
   if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || S < 1 || Hq % Hkv != 0 || (D != 64 && D != 128) ||
       L > PFA_DECODE_MAX_L || S > PFA_MAX_LEN || B > (1 << 20) || Hq > (1 << 20))
@@ -252,7 +313,7 @@ int prefill_attn_gqa_decode(const void* Q, const void* K, const void* V, int B, 
 const char* pfa_status_str(int status) {
   switch (status) {
     case PFA_OK: return "ok";
-    case PFA_ERR_NULL: return "null pointer (Q, K, V, O and, for varlen, both prefix sums, for decode the workspace)";
+    case PFA_ERR_NULL: return "null pointer (every tensor of the call; varlen prefix sums; the decode workspace)";
     case PFA_ERR_SIZE: return "invalid size: B, Hq, Hkv, L, S, D must be >= 1 and fit the launch";
     case PFA_ERR_GQA: return "Hq must be a multiple of Hkv";
     case PFA_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
@@ -263,6 +324,7 @@ const char* pfa_status_str(int status) {
     case PFA_ERR_FLAGS: return "unknown flag bit";
     case PFA_ERR_LAUNCH: return "HIP kernel launch failed (is a gfx950 device current?)";
     case PFA_ERR_WORKSPACE: return "workspace smaller than pfa_decode_workspace_bytes() for this shape";
+    case PFA_ERR_RING: return "ring cache must have >= 64 slots and hold every visible key (window - 1 + L, or pos0 + L without a window)";
     default: return "unknown status";
   }
 }

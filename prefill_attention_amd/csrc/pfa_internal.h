@@ -26,6 +26,8 @@ struct Launch {
   const int* cu_q = nullptr;
   const int* cu_k = nullptr;
   int total_q = 0, total_k = 0;
+  // Rotating cache (0 = off): K / V are [batch, hkv, ring, d], key position j in slot j mod ring.
+  int ring = 0;
 };
 
 // Query rows handled by one workgroup of the prefill kernel.
@@ -36,6 +38,10 @@ long long grid_blocks(const Launch& p);
 
 // Enqueue the prefill kernel. Returns PFA_OK or PFA_ERR_LAUNCH.
 int launch_prefill(const Launch& p);
+
+// Enqueue the rotating-cache append (K_new / V_new rows to slots (pos0 + i) mod ring).
+int launch_ring_append(const void* k_new, const void* v_new, void* k_ring, void* v_ring, int B, int Hkv, int L,
+                       int D, int ring, int pos0, void* stream);
 
 // Work split of the short-query (decode) path, a pure function of the shape so that the
 // workspace query and the launch agree: the rows of one KV head (G * L) in row groups of up to 64,

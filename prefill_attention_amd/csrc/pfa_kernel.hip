@@ -103,6 +103,9 @@ struct Params {
   const int* cu_q;
   const int* cu_k;
   int total_q, total_k;
+  // Rotating (ring) cache, dense layout only (0 = off): K / V are [B, Hkv, ring, D] and key
+  // position j lives in slot j mod ring.
+  int ring;
   int no_skip;
   int batch;
   int n_qblk;
@@ -184,7 +187,7 @@ __device__ void key_mask_chunk(const uint8_t* mrow, int S, int t0, int lane, uin
   *all = __ballot(al);
 }
 
-template <int D, bool KMASK>
+template <int D, bool KMASK, bool RING>
 __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   using G = Geo<D>;
   constexpr int KQ = G::KQ;
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     S = p.sk;
     causal_offset = p.causal_offset;
     q_base = ((long long)b * p.hq + h) * (long long)L * D;
-    kv_base = ((long long)b * p.hkv + hk) * (long long)S * D;
+    kv_base = ((long long)b * p.hkv + hk) * (long long)(RING ? p.ring : S) * D;
     q_stride = D;
     kv_stride = D;
   } else {
@@ -360,15 +363,34 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   auto issue = [&](int kt, int st) __attribute__((always_inline)) {
     const long long key0 = (long long)kt * kBN;
     const long long rows = (long long)S - key0;
-    const int nrec = (rows < kBN ? (int)rows : kBN) * 2 * kv_stride;
-    const uintptr_t base = reinterpret_cast<uintptr_t>(dma_src + key0 * kv_stride);
+    constexpr bool ring = RING;  // rotating cache (p.ring slots)
+    // ring cache: the descriptor covers the whole ring
+    const int nrec = ring ? p.ring * G::kRowBytes : (rows < kBN ? (int)rows : kBN) * 2 * kv_stride;
+    const uintptr_t base = reinterpret_cast<uintptr_t>(ring ? dma_src : dma_src + key0 * kv_stride);
     // readfirstlane returns int: go through unsigned so the low word is not sign-extended
     const unsigned base_hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(base >> 32));
     const unsigned base_lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)base);
     const uintptr_t base_u = ((uintptr_t)base_hi << 32) | (uintptr_t)base_lo;
     lds_char* dst = (lds_char*)lds_raw + st * G::kStageBytes + dma_lds;
-    dma_rows<G::kDmaPerWave>(reinterpret_cast<const void*>(base_u), __builtin_amdgcn_readfirstlane(nrec),
-                             dst, dma_off);
+    if constexpr (!ring) {
+      dma_rows<G::kDmaPerWave>(reinterpret_cast<const void*>(base_u), __builtin_amdgcn_readfirstlane(nrec),
+                               dst, dma_off);
+    } else {
+      // row r of the tile (position key0 + r) is slot (key0 mod ring) + r, wrapped once
+      // (ring >= 64 > r); rows at positions past S read as zeros (offset at the descriptor's end)
+      const int slot0 = (int)(key0 % p.ring);
+      unsigned off[G::kDmaPerWave];
+#pragma unroll
+      for (int j = 0; j < G::kDmaPerWave; ++j) {
+        const int row = (w4 * G::kDmaPerWave + j) * G::kRowsPerDma + lane / G::kChunksPerRow;
+        int slot = slot0 + row;
+        if (slot >= p.ring) slot -= p.ring;
+        const unsigned in_row = dma_off[j] - (unsigned)(row * G::kRowBytes);
+        off[j] = (row < rows) ? (unsigned)(slot * G::kRowBytes) + in_row : (unsigned)nrec;
+      }
+      dma_rows<G::kDmaPerWave>(reinterpret_cast<const void*>(base_u), __builtin_amdgcn_readfirstlane(nrec),
+                               dst, off);
+    }
     if (kmask && tid < kBN) mreg = (key0 + tid < S) ? mrow[key0 + tid] : (uint8_t)0;
   };
   // wait for this wave's fetches; waves 0-3 also publish the tile's mask bytes
@@ -696,23 +718,54 @@ int launch_variant(const pfa::Launch& L) {
   p.total_k = L.total_k;
   p.window = L.window;
   p.no_skip = (L.flags & PFA_FLAG_NO_SKIP) ? 1 : 0;
+  p.ring = L.ring;
   p.batch = L.batch;
   p.n_qblk = (L.lq + kBM - 1) / kBM;
   const long long n = (long long)L.batch * L.hq * p.n_qblk;
   p.n_wg = (int)n;
   p.xcd_remap = (n % kXcds) == 0 ? 1 : 0;
   void* args[] = {&p};
-  const void* fn = L.key_mask ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, true>)
-                             : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, false>);
+  const void* fn = L.ring       ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, false, true>)
+                   : L.key_mask ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, true, false>)
+                                : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, false, false>);
   hipError_t e = hipLaunchKernel(fn,
                                  dim3((unsigned)n), dim3(kThreads), args, 0,
                                  static_cast<hipStream_t>(L.stream));
   return e == hipSuccess ? PFA_OK : PFA_ERR_LAUNCH;
 }
 
+// Rotating-cache append: row i of K_new / V_new [B, Hkv, L, D] (position pos0 + i) goes to slot
+// (pos0 + i) mod ring of K_ring / V_ring [B, Hkv, ring, D]. One thread per 16 bytes.
+__global__ __launch_bounds__(256) void pfa_ring_append_kernel(const uint4* __restrict__ kn, const uint4* __restrict__ vn,
+                                                              uint4* __restrict__ kr, uint4* __restrict__ vr,
+                                                              long long n_chunks, int L, int ring, int pos0,
+                                                              int chunks_per_row) {
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_chunks) return;
+  const int c = (int)(t % chunks_per_row);
+  long long r = t / chunks_per_row;  // (b * Hkv + hk) * L + i
+  const int i = (int)(r % L);
+  const long long bh = r / L;
+  const long long slot = ((long long)pos0 + i) % ring;
+  const long long dst = (bh * ring + slot) * chunks_per_row + c;
+  kr[dst] = kn[t];
+  vr[dst] = vn[t];
+}
+
 }  // namespace
 
 namespace pfa {
+
+int launch_ring_append(const void* k_new, const void* v_new, void* k_ring, void* v_ring, int B, int Hkv, int L,
+                       int D, int ring, int pos0, void* stream) {
+  const int cpr = D / 8;
+  const long long n = (long long)B * Hkv * L * cpr;
+  const long long blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(pfa_ring_append_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new), static_cast<uint4*>(k_ring),
+                     static_cast<uint4*>(v_ring), n, L, ring, pos0, cpr);
+  return hipGetLastError() == hipSuccess ? PFA_OK : PFA_ERR_LAUNCH;
+}
 
 int rows_per_block(int) { return kBM; }
 

@@ -223,3 +223,38 @@ def test_decode_workspace_bytes_function(lib):
     # a pure function of the shape, growing with the rows kept per partial
     assert pfa.decode_workspace_bytes(1, 32, 8, 4, 4096, 128) == pfa.decode_workspace_bytes(1, 32, 8, 4, 4096, 128)
     assert pfa.decode_workspace_bytes(1, 32, 8, 8, 4096, 128) > pfa.decode_workspace_bytes(1, 32, 8, 1, 4096, 128)
+
+
+# ---- rotating-cache entry point ----
+KN, VN, KR, VR = 9 * A, 10 * A, 11 * A, 12 * A
+RGOOD = dict(q=Q, kn=KN, vn=VN, kr=KR, vr=VR, B=1, Hq=8, Hkv=2, L=16, pos0=5000, ring=1088, D=128,
+             scale=0.088, window=1024, o=O, stream=None)
+
+
+def rcall(**kw):
+    a = dict(RGOOD)
+    a.update(kw)
+    return pfa.prefill_attn_gqa_ring_raw(a["q"], a["kn"], a["vn"], a["kr"], a["vr"], a["B"], a["Hq"], a["Hkv"],
+                                         a["L"], a["pos0"], a["ring"], a["D"], a["scale"], a["window"], a["o"],
+                                         a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(kn=0), 1), (dict(vr=0), 1), (dict(o=0), 1),
+    (dict(L=0), 2), (dict(pos0=-1), 2), (dict(ring=0), 2), (dict(pos0=2 ** 30), 2),
+    (dict(Hq=6, Hkv=4), 3), (dict(D=96), 4), (dict(scale=float("nan")), 6),
+    (dict(ring=1038), 12),                      # < window - 1 + L = 1039
+    (dict(ring=63, window=8, L=4), 12),         # < 64 slots
+    (dict(window=0, ring=4096), 12),            # no window: needs pos0 + L = 5016 slots
+    (dict(kr=KR + 2), 7), (dict(o=O + 8), 7),
+    (dict(kr=Q), 8), (dict(vr=KN + 64), 8), (dict(o=KR), 8), (dict(kr=VR - 1024), 8),
+], ids=lambda x: str(x))
+def test_ring_invalid_arguments_rejected(lib, kw, code):
+    assert rcall(**kw) == code
+
+
+def test_ring_capacity_rule_counts_only_existing_keys(lib):
+    # pos0 + L <= ring: every key fits even though window - 1 + L would not; the next error after the
+    # capacity check is an alias planted on purpose
+    assert rcall(pos0=100, L=16, window=4096, ring=128, o=Q) == 8
+    assert rcall(pos0=200, L=16, window=4096, ring=128, o=Q) == 12

@@ -44,6 +44,11 @@ CONFIGS: dict[str, dict] = {
     # Batched bidirectional prefill with per-sequence key padding (encoder-style prefill).
     "bidir_padded_b8": dict(B=8, Hq=32, Hkv=8, D=128, L=4096, S=4096, causal_offset=NO_CAUSAL,
                             window=0, amp=1.0, key_padding=(1024, 4096)),
+    # The sliding-window chunk through the rotating-cache entry point: the first 1023 keys are the
+    # cached history (in a 3072-slot ring, key j in slot j mod 3072), the last 2048 the chunk's own
+    # keys, appended by the call (TensorFold PR: ring slot of a key row; brotensor kv_cache_append).
+    "ring_w1024_l2048": dict(B=1, Hq=32, Hkv=8, D=128, L=2048, S=3071, causal_offset=1023, window=1024,
+                             amp=1.0, key_padding=None, entry="ring", ring=3072),
     # Short-query chunks for the decode entry point (tiny-llm Task 2 routes one-token decode and
     # L <= 8 to a separate path; brotensor flash_attention_decode: query position valid_len - L + i).
     "decode_l1_32k": dict(B=1, Hq=32, Hkv=8, D=128, L=1, S=32768, causal_offset=32767, window=0,
