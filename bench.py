@@ -43,6 +43,7 @@ WORKLOADS = {
     "small_prompt_128": ["small_prompt_128"],
     "causal_witness_33x47": ["causal_witness_33x47"],
     "varlen_causal_b8": ["varlen_causal_b8"],
+    "long_ctx_32k_softcap50": ["long_ctx_32k_softcap50"],
     "ring_w1024_l2048": ["ring_w1024_l2048"],
     "decode_l1_32k": ["decode_l1_32k"],
     "decode_l8_8k": ["decode_l8_8k"],
@@ -280,6 +281,8 @@ def main() -> int:
         kw = dict(scale=float(x["scale"]), causal=causal,
                   causal_offset=x["causal_offset"] if causal else None, window=x["window"],
                   key_mask=m, out=out)
+        if c.get("softcap"):
+            kw["softcap"] = float(c["softcap"])
         if c.get("entry") == "decode":
             kw["workspace"] = torch.empty(pfa.decode_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["S"], c["D"]),
                                           dtype=torch.uint8, device=dev)

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define PFA_VERSION 10300 /* 1.3.0 */
+#define PFA_VERSION 10400 /* 1.4.0 */
 
 /* causal_offset < 0 selects bidirectional attention (no causal term). */
 #define PFA_NO_CAUSAL (-1)
@@ -67,7 +67,7 @@ enum pfa_status {
   PFA_ERR_GQA = 3,       /* Hq is not a multiple of Hkv                                         */
   PFA_ERR_HEAD_DIM = 4,  /* D is not 64 or 128                                                  */
   PFA_ERR_MASK_ARGS = 5, /* window > 0 without the causal term                                  */
-  PFA_ERR_SCALE = 6,     /* scale is not finite or not > 0                                      */
+  PFA_ERR_SCALE = 6,     /* scale not finite or not > 0; softcap not finite or < 0              */
   PFA_ERR_ALIGN = 7,     /* Q, K, V or O not 16-byte aligned (prefix sums: not 4-byte aligned)  */
   PFA_ERR_ALIAS = 8,     /* O (or the decode workspace) overlaps another buffer of the call     */
   PFA_ERR_FLAGS = 9,     /* unknown bit in flags                                                */
@@ -111,6 +111,28 @@ int prefill_attn_gqa_ex(const void* Q, const void* K, const void* V,
                         float scale, int causal_offset, int window,
                         const uint8_t* key_mask, void* O, void* stream,
                         unsigned flags);
+
+/*
+ * Options of prefill_attn_gqa_opt / prefill_attn_gqa_decode_opt. A zero-filled struct (or a NULL
+ * pointer) is the plain call.
+ *
+ *   flags    0 or PFA_FLAG_NO_SKIP (prefill only; the decode path rejects it with PFA_ERR_FLAGS)
+ *   softcap  > 0: logit soft-capping (brotensor flash_attention_decode, attn_softcap, the Gemma-2
+ *            extension): after the scale and before the masks and the softmax, every score s
+ *            becomes softcap * tanh(s / softcap). 0 = off. Must be finite and >= 0
+ *            (PFA_ERR_SCALE otherwise).
+ */
+typedef struct pfa_options {
+  unsigned flags;
+  float softcap;
+} pfa_options;
+
+/* prefill_attn_gqa_ex with options (see pfa_options). */
+int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V,
+                         int B, int Hq, int Hkv, int L, int S, int D,
+                         float scale, int causal_offset, int window,
+                         const uint8_t* key_mask, void* O, void* stream,
+                         const pfa_options* opts);
 
 /*
  * prefill_attn_gqa_varlen -- the same attention over a packed batch of variable-length sequences
@@ -205,6 +227,14 @@ int prefill_attn_gqa_decode(const void* Q, const void* K, const void* V,
                             float scale, int causal_offset, int window,
                             const uint8_t* key_mask, void* O,
                             void* workspace, int64_t workspace_bytes, void* stream);
+
+/* prefill_attn_gqa_decode with options (see pfa_options; flags must be 0). */
+int prefill_attn_gqa_decode_opt(const void* Q, const void* K, const void* V,
+                                int B, int Hq, int Hkv, int L, int S, int D,
+                                float scale, int causal_offset, int window,
+                                const uint8_t* key_mask, void* O,
+                                void* workspace, int64_t workspace_bytes, void* stream,
+                                const pfa_options* opts);
 
 /* Workspace bytes prefill_attn_gqa_decode needs for this shape (a pure function of the
  * arguments), or -1 if the shape is invalid for it. */

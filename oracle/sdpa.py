@@ -24,6 +24,9 @@ Definition implemented (one batch element b, one query head h):
     - always ``j < S``.
 * ``A[i, j] = 0`` if vis else ``-inf``; ``scores = scale * Q K^T + A``;
   ``O[i] = softmax(scores[i]) V``.
+* Optional logit soft-capping (brotensor ``flash_attention_decode``, ``attn_softcap``: after the
+  scale and before the mask and the softmax, each score ``s`` becomes ``cap * tanh(s / cap)``):
+  ``scores = cap * tanh(scale * Q K^T / cap) + A`` when ``softcap = cap > 0``.
 * A row with no visible key has no probability mass and its output is all zeros
   (tiny-llm Task 2).
 
@@ -110,12 +113,19 @@ def _softmax_rows_times_v(scores: np.ndarray, v: np.ndarray) -> np.ndarray:
     return out
 
 
+def soft_cap(scores: np.ndarray, softcap: float) -> np.ndarray:
+    """cap * tanh(scores / cap) for cap > 0 (brotensor attn_softcap); identity for cap == 0."""
+    if softcap > 0.0:
+        return softcap * np.tanh(scores / softcap)
+    return scores
+
+
 def attention_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.ndarray,
                    scale: float, causal_offset: int, window: int,
-                   key_valid: np.ndarray | None) -> np.ndarray:
+                   key_valid: np.ndarray | None, softcap: float = 0.0) -> np.ndarray:
     """Output rows for one (b, h): q_rows [n, D] at query positions `rows`, k/v [S, D] (fp64)."""
     S = k.shape[0]
-    scores = float(scale) * (q_rows @ k.T)
+    scores = soft_cap(float(scale) * (q_rows @ k.T), float(softcap))
     scores = scores + additive_mask(rows, S, causal_offset, window, key_valid)
     return _softmax_rows_times_v(scores, v)
 
@@ -128,7 +138,7 @@ def _widen(x):
 
 def oracle_sdpa(q, k, v, scale, causal_offset: int = NO_CAUSAL, window: int = 0,
                 key_mask: np.ndarray | None = None, row_block: int = 256,
-                workers: int = 1) -> np.ndarray:
+                workers: int = 1, softcap: float = 0.0) -> np.ndarray:
     """Masked grouped-query SDPA in fp64.
 
     q: [B,Hq,L,D], k/v: [B,Hkv,S,D] as bf16 bits (uint16) or floats; key_mask: uint8 [B,S] or
@@ -148,7 +158,7 @@ def oracle_sdpa(q, k, v, scale, causal_offset: int = NO_CAUSAL, window: int = 0,
         rows = np.arange(r0, min(r0 + row_block, L))
         kv = None if key_mask is None else (key_mask[b] != 0)
         out[b, h, rows] = attention_rows(q[b, h, rows], k[b, hk], v[b, hk], rows, scale,
-                                         causal_offset, window, kv)
+                                         causal_offset, window, kv, softcap)
 
     if workers <= 1:
         for it in items:
@@ -159,7 +169,8 @@ def oracle_sdpa(q, k, v, scale, causal_offset: int = NO_CAUSAL, window: int = 0,
     return out
 
 
-def oracle_selected_rows(q, k, v, scale, causal_offset, window, key_mask, picks) -> np.ndarray:
+def oracle_selected_rows(q, k, v, scale, causal_offset, window, key_mask, picks,
+                         softcap: float = 0.0) -> np.ndarray:
     """Oracle output for selected (b, h, row) triples only: returns fp64 [len(picks), D].
 
     Used at full workload sizes, where computing every row would take too long."""
@@ -171,7 +182,7 @@ def oracle_selected_rows(q, k, v, scale, causal_offset, window, key_mask, picks)
         qr = _widen(q[b, h, i:i + 1])
         kv = None if key_mask is None else (key_mask[b] != 0)
         res.append(attention_rows(qr, kb, vb, np.array([i]), float(np.float64(scale)),
-                                  causal_offset, window, kv)[0])
+                                  causal_offset, window, kv, softcap)[0])
     return np.array(res)
 
 
@@ -190,8 +201,9 @@ def visible_pair_count(B, Hq, L, S, causal_offset, window, key_mask=None, row_bl
 # ----------------------------------------------------------------------------------------------
 # Brute force (pure Python scalars) for tiny cases
 # ----------------------------------------------------------------------------------------------
-def brute_sdpa(q, k, v, scale, causal_offset=NO_CAUSAL, window=0, key_mask=None):
-    """Scalar-loop SDPA on nested lists / small arrays, with math.exp. Shapes as oracle_sdpa."""
+def brute_sdpa(q, k, v, scale, causal_offset=NO_CAUSAL, window=0, key_mask=None, softcap=0.0):
+    """Scalar-loop SDPA on nested lists / small arrays, with math.exp (and math.tanh for the
+    soft-cap). Shapes as oracle_sdpa."""
     q, k, v = _widen(np.asarray(q)), _widen(np.asarray(k)), _widen(np.asarray(v))
     B, Hq, L, D = q.shape
     Hkv, S, Dv = k.shape[1], k.shape[2], v.shape[3]
@@ -212,7 +224,10 @@ def brute_sdpa(q, k, v, scale, causal_offset=NO_CAUSAL, window=0, key_mask=None)
                     s = 0.0
                     for d in range(D):
                         s += float(q[b, h, i, d]) * float(k[b, hk, j, d])
-                    keys.append((j, float(scale) * s))
+                    s = float(scale) * s
+                    if softcap > 0.0:
+                        s = softcap * math.tanh(s / softcap)
+                    keys.append((j, s))
                 if not keys:
                     continue
                 mx = max(s for _, s in keys)

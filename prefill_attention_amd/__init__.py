@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     MAX_LEN,
     NO_CAUSAL,
+    Options,
     STATUS,
     PfaError,
     decode_workspace_bytes,

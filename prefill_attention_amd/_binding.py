@@ -23,8 +23,14 @@ STATUS = {
     9: "PFA_ERR_FLAGS", 10: "PFA_ERR_LAUNCH", 11: "PFA_ERR_WORKSPACE", 12: "PFA_ERR_RING",
 }
 DECODE_MAX_L = 64
-EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_varlen", "prefill_attn_gqa_ring",
-           "prefill_attn_gqa_decode", "pfa_decode_workspace_bytes", "pfa_status_str", "pfa_version")
+EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_opt", "prefill_attn_gqa_varlen",
+           "prefill_attn_gqa_ring", "prefill_attn_gqa_decode", "prefill_attn_gqa_decode_opt",
+           "pfa_decode_workspace_bytes", "pfa_status_str", "pfa_version")
+
+
+class Options(ctypes.Structure):
+    """Mirror of struct pfa_options."""
+    _fields_ = [("flags", ctypes.c_uint), ("softcap", ctypes.c_float)]
 
 _lib = None
 
@@ -50,11 +56,15 @@ def library() -> ctypes.CDLL:
         lib.prefill_attn_gqa.restype = ci
         lib.prefill_attn_gqa_ex.argtypes = sig + [cu]
         lib.prefill_attn_gqa_ex.restype = ci
+        lib.prefill_attn_gqa_opt.argtypes = sig + [ctypes.POINTER(Options)]
+        lib.prefill_attn_gqa_opt.restype = ci
         lib.prefill_attn_gqa_varlen.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, ci,
                                                 vp, vp]
         lib.prefill_attn_gqa_varlen.restype = ci
         lib.prefill_attn_gqa_decode.argtypes = sig[:-1] + [vp, ctypes.c_int64, vp]
         lib.prefill_attn_gqa_decode.restype = ci
+        lib.prefill_attn_gqa_decode_opt.argtypes = sig[:-1] + [vp, ctypes.c_int64, vp, ctypes.POINTER(Options)]
+        lib.prefill_attn_gqa_decode_opt.restype = ci
         lib.pfa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
         lib.pfa_decode_workspace_bytes.restype = ctypes.c_int64
         lib.prefill_attn_gqa_ring.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp, vp]
@@ -78,22 +88,28 @@ def version() -> int:
 def prefill_attn_gqa_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: int, Hkv: int, L: int,
                          S: int, D: int, scale: float, causal_offset: int, window: int,
                          key_mask_ptr: int | None, o_ptr: int, stream: int | None,
-                         flags: int = 0) -> int:
+                         flags: int = 0, softcap: float = 0.0) -> int:
     """Direct C-ABI call with integer pointers; returns the status code."""
-    return int(library().prefill_attn_gqa_ex(
+    if softcap == 0.0:
+        return int(library().prefill_attn_gqa_ex(
+            q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
+            key_mask_ptr or None, o_ptr, stream or None, flags))
+    opts = Options(flags, softcap)
+    return int(library().prefill_attn_gqa_opt(
         q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
-        key_mask_ptr or None, o_ptr, stream or None, flags))
+        key_mask_ptr or None, o_ptr, stream or None, ctypes.byref(opts)))
 
 
 def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True,
                      causal_offset: int | None = None, window: int = 0, key_mask=None, out=None,
-                     no_skip: bool = False, stream=None):
+                     no_skip: bool = False, softcap: float = 0.0, stream=None):
     """Grouped-query prefill attention on torch tensors.
 
     q: bf16 [B,Hq,L,D]; k, v: bf16 [B,Hkv,S,D]; key_mask: optional uint8/bool [B,S] (nonzero =
     valid). scale defaults to 1/sqrt(D). With causal=True the causal offset defaults to S - L
     (the chunk is the tail of the S keys); causal=False is bidirectional. window > 0 adds a
-    sliding window of that many keys. Returns `out` (allocated if None), bf16 [B,Hq,L,D].
+    sliding window of that many keys. softcap > 0 applies logit soft-capping. Returns `out`
+    (allocated if None), bf16 [B,Hq,L,D].
     """
     import torch
 
@@ -149,7 +165,7 @@ def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True
     with torch.cuda.device(q.device):
         rc = prefill_attn_gqa_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
                                   float(scale), int(causal_offset), int(window), mask_ptr,
-                                  out.data_ptr(), stream_ptr, FLAG_NO_SKIP if no_skip else 0)
+                                  out.data_ptr(), stream_ptr, FLAG_NO_SKIP if no_skip else 0, float(softcap))
     if rc != 0:
         raise PfaError(rc, status_str(rc))
     return out
@@ -225,16 +241,21 @@ def decode_workspace_bytes(B: int, Hq: int, Hkv: int, L: int, S: int, D: int) ->
 def prefill_attn_gqa_decode_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: int, Hkv: int, L: int,
                                 S: int, D: int, scale: float, causal_offset: int, window: int,
                                 key_mask_ptr: int | None, o_ptr: int, ws_ptr: int | None, ws_bytes: int,
-                                stream: int | None) -> int:
+                                stream: int | None, softcap: float = 0.0, flags: int = 0) -> int:
     """Direct C-ABI call of the short-query (decode) entry point; returns the status code."""
-    return int(library().prefill_attn_gqa_decode(
+    if softcap == 0.0 and flags == 0:
+        return int(library().prefill_attn_gqa_decode(
+            q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
+            key_mask_ptr or None, o_ptr, ws_ptr or None, ws_bytes, stream or None))
+    opts = Options(flags, softcap)
+    return int(library().prefill_attn_gqa_decode_opt(
         q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
-        key_mask_ptr or None, o_ptr, ws_ptr or None, ws_bytes, stream or None))
+        key_mask_ptr or None, o_ptr, ws_ptr or None, ws_bytes, stream or None, ctypes.byref(opts)))
 
 
 def prefill_attn_gqa_decode(q, k, v, *, scale: float | None = None, causal: bool = True,
                             causal_offset: int | None = None, window: int = 0, key_mask=None, out=None,
-                            workspace=None, stream=None):
+                            workspace=None, softcap: float = 0.0, stream=None):
     """Short-query (decode, L <= 64) grouped-query attention on torch tensors: the same arguments
     and result as prefill_attn_gqa, computed with the key range split over the chip and a
     deterministic merge. `workspace` is an optional uint8 GPU tensor of at least
@@ -285,7 +306,8 @@ def prefill_attn_gqa_decode(q, k, v, *, scale: float | None = None, causal: bool
     with torch.cuda.device(q.device):
         rc = prefill_attn_gqa_decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
                                          float(scale), int(causal_offset), int(window), mask_ptr,
-                                         out.data_ptr(), workspace.data_ptr(), workspace.numel(), stream_ptr)
+                                         out.data_ptr(), workspace.data_ptr(), workspace.numel(), stream_ptr,
+                                         float(softcap))
     if rc != 0:
         raise PfaError(rc, status_str(rc))
     return out

@@ -69,12 +69,15 @@ int validate(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv
 
 extern "C" {
 
-int prefill_attn_gqa_ex(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv,
-                        int L, int S, int D, float scale, int causal_offset, int window,
-                        const uint8_t* key_mask, void* O, void* stream, unsigned flags) {
+int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv,
+                         int L, int S, int D, float scale, int causal_offset, int window,
+                         const uint8_t* key_mask, void* O, void* stream, const pfa_options* opts) {
+  const unsigned flags = opts ? opts->flags : 0u;
+  const float softcap = opts ? opts->softcap : 0.0f;
   int rc = validate(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window, key_mask, O,
                     flags);
   if (rc != PFA_OK) return rc;
+  if (!std::isfinite(softcap) || softcap < 0.0f) return PFA_ERR_SCALE;
   pfa::Launch p;
   p.q = Q;
   p.k = K;
@@ -94,8 +97,18 @@ int prefill_attn_gqa_ex(const void* Q, const void* K, const void* V, int B, int 
   p.window = (causal_offset >= 0 && window > 0) ? window : 0;
   p.flags = flags;
   p.stream = stream;
+  p.softcap = softcap;
   if (pfa::grid_blocks(p) > INT_MAX) return PFA_ERR_SIZE;
   return pfa::launch_prefill(p);
+}
+
+int prefill_attn_gqa_ex(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv,
+                        int L, int S, int D, float scale, int causal_offset, int window,
+                        const uint8_t* key_mask, void* O, void* stream, unsigned flags) {
+  pfa_options o{};
+  o.flags = flags;
+  return prefill_attn_gqa_opt(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window, key_mask, O,
+                              stream, &o);
 }
 
 int prefill_attn_gqa(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L,
@@ -263,12 +276,16 @@ int64_t pfa_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D) 
   return pfa::decode_plan(B, Hq, Hkv, L, S, D).workspace_bytes;
 }
 
-int prefill_attn_gqa_decode(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L,
-                            int S, int D, float scale, int causal_offset, int window,
-                            const uint8_t* key_mask, void* O, void* workspace, int64_t workspace_bytes,
-                            void* stream) {
-  int rc = validate(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window, key_mask, O, 0u);
+int prefill_attn_gqa_decode_opt(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L,
+                                int S, int D, float scale, int causal_offset, int window,
+                                const uint8_t* key_mask, void* O, void* workspace, int64_t workspace_bytes,
+                                void* stream, const pfa_options* opts) {
+  const unsigned flags = opts ? opts->flags : 0u;
+  const float softcap = opts ? opts->softcap : 0.0f;
+  int rc = validate(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window, key_mask, O, flags);
   if (rc != PFA_OK) return rc;
+  if (flags != 0u) return PFA_ERR_FLAGS;
+  if (!std::isfinite(softcap) || softcap < 0.0f) return PFA_ERR_SCALE;
   if (!workspace) return PFA_ERR_NULL;
   if (L > PFA_DECODE_MAX_L || B > (1 << 20) || Hq > (1 << 20)) return PFA_ERR_SIZE;
   const pfa::DecodePlan plan = pfa::decode_plan(B, Hq, Hkv, L, S, D);
@@ -307,7 +324,16 @@ int prefill_attn_gqa_decode(const void* Q, const void* K, const void* V, int B, 
   p.window = (causal_offset >= 0 && window > 0) ? window : 0;
   p.flags = 0;
   p.stream = stream;
+  p.softcap = softcap;
   return pfa::launch_decode(p, plan, workspace);
+}
+
+int prefill_attn_gqa_decode(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L,
+                            int S, int D, float scale, int causal_offset, int window,
+                            const uint8_t* key_mask, void* O, void* workspace, int64_t workspace_bytes,
+                            void* stream) {
+  return prefill_attn_gqa_decode_opt(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window, key_mask, O,
+                                     workspace, workspace_bytes, stream, nullptr);
 }
 
 const char* pfa_status_str(int status) {

@@ -66,6 +66,7 @@ struct DParams {
   int hq, hkv, group, lq, sk;
   float c;
   int causal, causal_offset, window;
+  float sc_inv, sc_cap_l2;  // logit soft-capping: scale / cap and cap * log2(e)
   int n_rowgrp, rows_cap, n_split, tiles_per_split;
   long long n_partials;
 };
@@ -83,6 +84,15 @@ __device__ __forceinline__ float max_with_partner_half(float x) {
 // N DMA instructions from a buffer of nrec bytes at base (wave-uniform) into LDS: instruction j
 // writes lane l's 16 bytes, read from byte offset off[j], to LDS address dst + 1024 j + 16 l.
 // Reads at or past nrec return zeros.
+// log2(e) * cap * tanh(s * scale / cap) (inv = scale / cap, cap_l2 = cap * log2(e)) from
+// tanh(y) = sign(y) (1 - t) / (1 + t), t = e^(-2|y|) in (0, 1]
+__device__ __forceinline__ float softcap_l2(float s, float inv, float cap_l2) {
+  const float y = s * inv;
+  const float t = __builtin_amdgcn_exp2f(-2.0f * kLog2e * __builtin_fabsf(y));
+  const float th = (1.0f - t) * __builtin_amdgcn_rcpf(1.0f + t);
+  return __builtin_copysignf(th, y) * cap_l2;
+}
+
 template <int N>
 __device__ __forceinline__ void dma_rows(const void* base, int nrec, lds_char* dst, const unsigned* off) {
   __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nrec, kBufferFlags);
@@ -92,7 +102,7 @@ __device__ __forceinline__ void dma_rows(const void* base, int nrec, lds_char* d
                                              off[j], 0, 0, 0);
 }
 
-template <int D, int RB, bool KMASK>
+template <int D, int RB, bool KMASK, bool SOFTCAP>
 __global__ __launch_bounds__(64) void pfa_decode_split_kernel(DParams p) {
   using G = DGeo<D>;
   constexpr int KQ = G::KQ;
@@ -220,7 +230,8 @@ __global__ __launch_bounds__(64) void pfa_decode_split_kernel(DParams p) {
     m[rb] = -INFINITY;
     l[rb] = 0.0f;
   }
-  const float c = p.c;
+  // with soft-capping the scores are turned into the base-2 exponent domain up front
+  const float c = SOFTCAP ? 1.0f : p.c;
 
   if (t_begin < t_end) issue(t_begin, lds_raw);
   // One step: tile t is in `cur`, tile t+1 is fetched into `nxt`. The stages are restrict
@@ -242,6 +253,13 @@ __global__ __launch_bounds__(64) void pfa_decode_split_kernel(DParams p) {
       const bf16x8 a = *(const lds_bf16x8*)(base + (a_k ^ (32 * kk)));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[rb][kk], s[rb], 0, 0, 0);
+    }
+    if constexpr (SOFTCAP) {
+      // logit soft-capping before the masks (brotensor flash_attention_decode, attn_softcap)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[rb][v] = softcap_l2(s[rb][v], p.sc_inv, p.sc_cap_l2);
     }
     // mask: lane row's interval and the key bytes
     const int key0 = t * kTk;
@@ -439,6 +457,9 @@ int launch_decode_variant(const pfa::Launch& L, const pfa::DecodePlan& plan, voi
   p.causal = L.causal;
   p.causal_offset = L.causal_offset;
   p.window = L.window;
+  const bool sc = L.softcap > 0.0f;
+  p.sc_inv = sc ? L.scale / L.softcap : 0.0f;
+  p.sc_cap_l2 = sc ? L.softcap * kLog2e : 0.0f;
   p.n_rowgrp = plan.n_rowgrp;
   p.rows_cap = plan.rows_cap;
   p.n_split = plan.n_split;
@@ -446,8 +467,11 @@ int launch_decode_variant(const pfa::Launch& L, const pfa::DecodePlan& plan, voi
   p.n_partials = plan.n_partials;
   hipStream_t stream = static_cast<hipStream_t>(L.stream);
   void* args[] = {&p};
-  const void* fn = L.key_mask ? reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, true>)
-                              : reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, false>);
+  const void* fn =
+      L.key_mask ? (sc ? reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, true, true>)
+                       : reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, true, false>))
+                 : (sc ? reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, false, true>)
+                       : reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, false, false>));
   if (hipLaunchKernel(fn, dim3((unsigned)plan.n_partials), dim3(64), args, 0, stream) != hipSuccess)
     return PFA_ERR_LAUNCH;
   uint16_t* o = static_cast<uint16_t*>(L.o);

@@ -28,6 +28,8 @@ struct Launch {
   int total_q = 0, total_k = 0;
   // Rotating cache (0 = off): K / V are [batch, hkv, ring, d], key position j in slot j mod ring.
   int ring = 0;
+  // Logit soft-capping (0 = off): each scaled score s becomes softcap * tanh(s / softcap).
+  float softcap = 0.0f;
 };
 
 // Query rows handled by one workgroup of the prefill kernel.

@@ -106,6 +106,7 @@ struct Params {
   // Rotating (ring) cache, dense layout only (0 = off): K / V are [B, Hkv, ring, D] and key
   // position j lives in slot j mod ring.
   int ring;
+  float sc_inv, sc_cap_l2;  // soft-capping: scale / cap and cap * log2(e)
   int no_skip;
   int batch;
   int n_qblk;
@@ -145,6 +146,16 @@ __device__ __forceinline__ float max_with_partner_half(float x) {
   unsigned a = __builtin_bit_cast(unsigned, x), b = a;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
   return max2(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
+// log2(e) * cap * tanh(s * scale / cap), with inv = scale / cap and cap_l2 = cap * log2(e):
+// tanh(y) = sign(y) (1 - t) / (1 + t), t = e^(-2|y|) in (0, 1], so nothing overflows and the
+// absolute error stays a few ulp of cap (the softmax needs the exponent to absolute accuracy).
+__device__ __forceinline__ float softcap_l2(float s, float inv, float cap_l2) {
+  const float y = s * inv;
+  const float t = __builtin_amdgcn_exp2f(-2.0f * kLog2e * __builtin_fabsf(y));
+  const float th = (1.0f - t) * __builtin_amdgcn_rcpf(1.0f + t);
+  return __builtin_copysignf(th, y) * cap_l2;
 }
 
 __device__ __forceinline__ bool any_zero_byte(uint32_t x) {
@@ -187,8 +198,16 @@ __device__ void key_mask_chunk(const uint8_t* mrow, int S, int t0, int lane, uin
   *all = __ballot(al);
 }
 
-template <int D, bool KMASK, bool RING>
+// Kernel variants (template MODE bits): a key mask, a rotating cache, logit soft-capping.
+constexpr int kModeKeyMask = 1;
+constexpr int kModeRing = 2;
+constexpr int kModeSoftcap = 4;
+
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
+  constexpr bool KMASK = (MODE & kModeKeyMask) != 0;
+  constexpr bool RING = (MODE & kModeRing) != 0;
+  constexpr bool SOFTCAP = (MODE & kModeSoftcap) != 0;
   using G = Geo<D>;
   constexpr int KQ = G::KQ;
   constexpr int DB = G::DB;
@@ -306,7 +325,8 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   // key), l_run this lane's half of the row sum of P.
   float mref = -INFINITY;
   float l_run = 0.0f;
-  const float c = p.c;
+  // with soft-capping the scores are turned into the base-2 exponent domain up front
+  const float c = SOFTCAP ? 1.0f : p.c;
 
   // ---- key-mask bitmap (per wave, 64 tiles per chunk) ----
   int mchunk = -1;
@@ -512,6 +532,14 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
 
   // ---- the VALU phase: mask, online softmax, P in bf16, accumulator rescale ----
   auto softmax = [&](const TileView& tv, int st) __attribute__((always_inline)) {
+    if constexpr (SOFTCAP) {
+      // logit soft-capping before the masks and the softmax (brotensor flash_attention_decode,
+      // attn_softcap): x = log2(e) * cap * tanh(scale * s / cap)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kb][v] = softcap_l2(s[kb][v], p.sc_inv, p.sc_cap_l2);
+    }
     if (tv.need_mask) {
       // Row ii = l32 sees tile keys jj in [lo, lo + span] (causal, window and tail bounds),
       // tested as one unsigned compare per score; span < 0 means the row sees nothing.
@@ -725,9 +753,19 @@ int launch_variant(const pfa::Launch& L) {
   p.n_wg = (int)n;
   p.xcd_remap = (n % kXcds) == 0 ? 1 : 0;
   void* args[] = {&p};
-  const void* fn = L.ring       ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, false, true>)
-                   : L.key_mask ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, true, false>)
-                                : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, false, false>);
+  const bool sc = L.softcap > 0.0f;
+  p.sc_inv = sc ? L.scale / L.softcap : 0.0f;
+  p.sc_cap_l2 = sc ? L.softcap * kLog2e : 0.0f;
+  const void* fn;
+  if (L.ring)
+    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeRing | kModeSoftcap>)
+            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeRing>);
+  else if (L.key_mask)
+    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeKeyMask | kModeSoftcap>)
+            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeKeyMask>);
+  else
+    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeSoftcap>)
+            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, 0>);
   hipError_t e = hipLaunchKernel(fn,
                                  dim3((unsigned)n), dim3(kThreads), args, 0,
                                  static_cast<hipStream_t>(L.stream));

@@ -258,3 +258,30 @@ def test_ring_capacity_rule_counts_only_existing_keys(lib):
     # capacity check is an alias planted on purpose
     assert rcall(pos0=100, L=16, window=4096, ring=128, o=Q) == 8
     assert rcall(pos0=200, L=16, window=4096, ring=128, o=Q) == 12
+
+
+# ---- options (soft-capping) ----
+@pytest.mark.parametrize("softcap,code", [(float("nan"), 6), (float("inf"), 6), (-1.0, 6)])
+def test_softcap_rejected(lib, softcap, code):
+    a = dict(GOOD)
+    assert pfa.prefill_attn_gqa_raw(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["L"], a["S"], a["D"],
+                                    a["scale"], a["off"], a["window"], a["mask"], a["o"], a["stream"], 0,
+                                    softcap) == code
+    d = dict(DGOOD)
+    need = pfa.decode_workspace_bytes(d["B"], d["Hq"], d["Hkv"], d["L"], d["S"], d["D"])
+    assert pfa.prefill_attn_gqa_decode_raw(d["q"], d["k"], d["v"], d["B"], d["Hq"], d["Hkv"], d["L"], d["S"],
+                                           d["D"], d["scale"], d["off"], d["window"], d["mask"], d["o"], d["ws"],
+                                           need, d["stream"], softcap) == code
+
+
+def test_options_flags_checked(lib):
+    a = dict(GOOD)
+    # an unknown flag through the options struct, and any flag on the decode path
+    assert pfa.prefill_attn_gqa_raw(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["L"], a["S"], a["D"],
+                                    a["scale"], a["off"], a["window"], a["mask"], a["o"], a["stream"], 2, 5.0) == 9
+    d = dict(DGOOD)
+    need = pfa.decode_workspace_bytes(d["B"], d["Hq"], d["Hkv"], d["L"], d["S"], d["D"])
+    assert pfa.prefill_attn_gqa_decode_raw(d["q"], d["k"], d["v"], d["B"], d["Hq"], d["Hkv"], d["L"], d["S"],
+                                           d["D"], d["scale"], d["off"], d["window"], d["mask"], d["o"], d["ws"],
+                                           need, d["stream"], 0.0, 1) == 9
+    assert ctypes.sizeof(pfa.Options) == 8

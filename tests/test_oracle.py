@@ -204,7 +204,40 @@ def pin_brute_force():
         assert np.allclose(o, ob, atol=1e-13, rtol=0), (B, Hq, Hkv, L, S, D, off, W)
 
 
-PINS = [pin_two_key_sigmoid, pin_rows_sum_to_one, pin_uniform_v_returns_v, pin_window_reductions,
+
+def pin_softcap():
+    """Logit soft-capping (brotensor attn_softcap): the two-key sigmoid identity on capped scores,
+    scalar brute force (math.tanh) on random masked cases, the large-cap limit (no cap) and the
+    small-cap limit (capped scores all near 0: the mean of the visible values)."""
+    sig = lambda x: 1.0 / (1.0 + math.exp(-x))
+    rng = np.random.default_rng(17)
+    for cap in (0.5, 2.0, 30.0):
+        q = rng.standard_normal((1, 1, 1, 3))
+        k = rng.standard_normal((1, 1, 2, 3)) * 4.0
+        v = rng.standard_normal((1, 1, 2, 3))
+        scale = 0.8
+        s0, s1 = scale * float(q[0, 0, 0] @ k[0, 0, 0]), scale * float(q[0, 0, 0] @ k[0, 0, 1])
+        d = cap * math.tanh(s1 / cap) - cap * math.tanh(s0 / cap)
+        ref = v[0, 0, 0] + sig(d) * (v[0, 0, 1] - v[0, 0, 0])
+        got = oracle_sdpa(q, k, v, scale, causal_offset=-1, softcap=cap)
+        assert np.allclose(got[0, 0, 0], ref, atol=1e-13, rtol=0)
+    for cap, off, W in [(1.0, 2, 0), (5.0, 0, 3), (0.3, -1, 0)]:
+        q = rng.standard_normal((1, 2, 4, 5)) * 3.0
+        k = rng.standard_normal((1, 1, 6, 5))
+        v = rng.standard_normal((1, 1, 6, 5))
+        got = oracle_sdpa(q, k, v, 0.6, causal_offset=off, window=W, softcap=cap)
+        ref = brute_sdpa(q, k, v, 0.6, causal_offset=off, window=W, softcap=cap)
+        assert np.allclose(got, ref, atol=1e-12, rtol=0)
+    q = rng.standard_normal((1, 2, 8, 16))
+    k = rng.standard_normal((1, 2, 20, 16))
+    v = rng.standard_normal((1, 2, 20, 16))
+    plain = oracle_sdpa(q, k, v, 0.25, causal_offset=12)
+    assert np.allclose(oracle_sdpa(q, k, v, 0.25, causal_offset=12, softcap=1e7), plain, atol=1e-10, rtol=0)
+    tiny = oracle_sdpa(q, k, v, 0.25, causal_offset=12, softcap=1e-9)
+    for i in range(8):
+        assert np.allclose(tiny[0, :, i], v[0, :, : i + 13].mean(axis=1), atol=1e-7, rtol=0)
+
+PINS = [pin_softcap, pin_two_key_sigmoid, pin_rows_sum_to_one, pin_uniform_v_returns_v, pin_window_reductions,
         pin_gqa_is_expanded_mha, pin_triu_counts, pin_zero_scale_prefix_means, pin_chunk_equals_tail,
         pin_key_padding, pin_brute_force]
 
@@ -359,8 +392,22 @@ def _bad_key_mask(rows, S, off, W, kv):
 osdpa_visible_orig = osdpa.visible
 
 
-def _bad_scale(q_rows, k, v, rows, scale, off, W, kv):
-    return _attention_rows_orig(q_rows, k, v, rows, 1.0, off, W, kv)
+def _bad_scale(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0):
+    return _attention_rows_orig(q_rows, k, v, rows, 1.0, off, W, kv, softcap)
+
+
+def _bad_softcap_after_mask(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0):
+    # the soft-cap applied after the mask: masked keys (-inf) become -cap, i.e. visible
+    S = k.shape[0]
+    scores = float(scale) * (q_rows @ k.T) + osdpa.additive_mask(rows, S, off, W, kv)
+    if softcap > 0:
+        scores = softcap * np.tanh(scores / softcap)
+    return osdpa._softmax_rows_times_v(scores, v)
+
+
+def _bad_softcap_unscaled(scores, softcap):
+    # tanh of the score without dividing by the cap
+    return softcap * np.tanh(scores) if softcap > 0 else scores
 
 
 def _bad_empty_rows(scores, v):
@@ -375,9 +422,11 @@ _attention_rows_orig = osdpa.attention_rows
 @pytest.mark.parametrize("attr,bad", [("kv_head_of", _bad_head_map), ("visible", _bad_causal),
                                       ("visible", _bad_window), ("visible", _bad_key_mask),
                                       ("attention_rows", _bad_scale),
-                                      ("_softmax_rows_times_v", _bad_empty_rows)],
+                                      ("_softmax_rows_times_v", _bad_empty_rows),
+                                      ("attention_rows", _bad_softcap_after_mask),
+                                      ("soft_cap", _bad_softcap_unscaled)],
                          ids=["head_map_mod", "causal_plus_one", "window_plus_one", "key_mask_dropped",
-                              "scale_dropped", "empty_rows_nan"])
+                              "scale_dropped", "empty_rows_nan", "softcap_after_mask", "softcap_unscaled"])
 def test_planted_mistake_is_caught(monkeypatch, attr, bad):
     monkeypatch.setattr(osdpa, attr, bad)
     caught = 0

@@ -44,6 +44,10 @@ CONFIGS: dict[str, dict] = {
     # Batched bidirectional prefill with per-sequence key padding (encoder-style prefill).
     "bidir_padded_b8": dict(B=8, Hq=32, Hkv=8, D=128, L=4096, S=4096, causal_offset=NO_CAUSAL,
                             window=0, amp=1.0, key_padding=(1024, 4096)),
+    # The long-context chunk with logit soft-capping at 50 (the Gemma-2 attention cap; brotensor
+    # attn_softcap).
+    "long_ctx_32k_softcap50": dict(B=1, Hq=32, Hkv=8, D=128, L=2048, S=32768, causal_offset=30720, window=0,
+                                   amp=1.0, key_padding=None, softcap=50.0),
     # The sliding-window chunk through the rotating-cache entry point: the first 1023 keys are the
     # cached history (in a 3072-slot ring, key j in slot j mod 3072), the last 2048 the chunk's own
     # keys, appended by the call (TensorFold PR: ring slot of a key row; brotensor kv_cache_append).
