@@ -44,6 +44,7 @@ WORKLOADS = {
     "causal_witness_33x47": ["causal_witness_33x47"],
     "varlen_causal_b8": ["varlen_causal_b8"],
     "long_ctx_32k_softcap50": ["long_ctx_32k_softcap50"],
+    "mid_ctx_8k_bias": ["mid_ctx_8k_bias"],
     "ring_w1024_l2048": ["ring_w1024_l2048"],
     "decode_l1_32k": ["decode_l1_32k"],
     "decode_l8_8k": ["decode_l8_8k"],
@@ -98,7 +99,8 @@ def varlen_algorithmic_bytes(x: dict) -> int:
 def algorithmic_bytes(c: dict) -> int:
     B, Hq, Hkv, L, S, D = c["B"], c["Hq"], c["Hkv"], c["L"], c["S"], c["D"]
     mask = B * S if c.get("key_padding") else 0
-    return 2 * (B * Hq * L * D + 2 * B * Hkv * S * D + B * Hq * L * D) + mask
+    bias = 4 * L * S if c.get("bias") == "LS" else 0
+    return 2 * (B * Hq * L * D + 2 * B * Hkv * S * D + B * Hq * L * D) + mask + bias
 
 
 def kernel_sha() -> str:
@@ -283,6 +285,8 @@ def main() -> int:
                   key_mask=m, out=out)
         if c.get("softcap"):
             kw["softcap"] = float(c["softcap"])
+        if x.get("bias") is not None:
+            kw["bias"] = torch.from_numpy(x["bias"]).to(dev)
         if c.get("entry") == "decode":
             kw["workspace"] = torch.empty(pfa.decode_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["S"], c["D"]),
                                           dtype=torch.uint8, device=dev)

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define PFA_VERSION 10400 /* 1.4.0 */
+#define PFA_VERSION 10500 /* 1.5.0 */
 
 /* causal_offset < 0 selects bidirectional attention (no causal term). */
 #define PFA_NO_CAUSAL (-1)
@@ -121,10 +121,21 @@ int prefill_attn_gqa_ex(const void* Q, const void* K, const void* V,
  *            extension): after the scale and before the masks and the softmax, every score s
  *            becomes softcap * tanh(s / softcap). 0 = off. Must be finite and >= 0
  *            (PFA_ERR_SCALE otherwise).
+ *   bias     NULL, or an additive FP32 bias (tiny-llm Week 2 Day 5 Task 2: a broadcastable
+ *            additive array mask, applied before the online-softmax update): element
+ *            bias[b * bias_stride_b + h * bias_stride_h + i * bias_stride_l + j] is added to the
+ *            (soft-capped) scaled score of query head h, row i, key j; keys are contiguous and a
+ *            zero stride broadcasts (e.g. strides 0, 0, S for one [L, S] mask). Values are finite
+ *            or -inf. Prefill entry point only, not with a key mask (PFA_ERR_MASK_ARGS); the
+ *            pointer and the strides must be multiples of 16 bytes / 4 elements (PFA_ERR_ALIGN);
+ *            one (b, h) block, (L - 1) * bias_stride_l + S elements, must stay under 2^29
+ *            elements (PFA_ERR_SIZE); it must not overlap O (PFA_ERR_ALIAS).
  */
 typedef struct pfa_options {
   unsigned flags;
   float softcap;
+  const float* bias;
+  int64_t bias_stride_b, bias_stride_h, bias_stride_l;
 } pfa_options;
 
 /* prefill_attn_gqa_ex with options (see pfa_options). */

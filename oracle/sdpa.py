@@ -27,6 +27,9 @@ Definition implemented (one batch element b, one query head h):
 * Optional logit soft-capping (brotensor ``flash_attention_decode``, ``attn_softcap``: after the
   scale and before the mask and the softmax, each score ``s`` becomes ``cap * tanh(s / cap)``):
   ``scores = cap * tanh(scale * Q K^T / cap) + A`` when ``softcap = cap > 0``.
+* Optional additive bias (tiny-llm Task 2: a broadcastable additive array mask, applied before the
+  online-softmax update): ``scores = [soft-capped] scale * Q K^T + bias[b, h] + A``, ``bias``
+  broadcastable to ``[B, Hq, L, S]``.
 * A row with no visible key has no probability mass and its output is all zeros
   (tiny-llm Task 2).
 
@@ -122,10 +125,14 @@ def soft_cap(scores: np.ndarray, softcap: float) -> np.ndarray:
 
 def attention_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.ndarray,
                    scale: float, causal_offset: int, window: int,
-                   key_valid: np.ndarray | None, softcap: float = 0.0) -> np.ndarray:
-    """Output rows for one (b, h): q_rows [n, D] at query positions `rows`, k/v [S, D] (fp64)."""
+                   key_valid: np.ndarray | None, softcap: float = 0.0,
+                   bias_rows: np.ndarray | None = None) -> np.ndarray:
+    """Output rows for one (b, h): q_rows [n, D] at query positions `rows`, k/v [S, D] (fp64);
+    bias_rows: the additive bias of these rows, [n, S], or None."""
     S = k.shape[0]
     scores = soft_cap(float(scale) * (q_rows @ k.T), float(softcap))
+    if bias_rows is not None:
+        scores = scores + bias_rows
     scores = scores + additive_mask(rows, S, causal_offset, window, key_valid)
     return _softmax_rows_times_v(scores, v)
 
@@ -138,7 +145,7 @@ def _widen(x):
 
 def oracle_sdpa(q, k, v, scale, causal_offset: int = NO_CAUSAL, window: int = 0,
                 key_mask: np.ndarray | None = None, row_block: int = 256,
-                workers: int = 1, softcap: float = 0.0) -> np.ndarray:
+                workers: int = 1, softcap: float = 0.0, bias: np.ndarray | None = None) -> np.ndarray:
     """Masked grouped-query SDPA in fp64.
 
     q: [B,Hq,L,D], k/v: [B,Hkv,S,D] as bf16 bits (uint16) or floats; key_mask: uint8 [B,S] or
@@ -151,6 +158,8 @@ def oracle_sdpa(q, k, v, scale, causal_offset: int = NO_CAUSAL, window: int = 0,
     out = np.zeros((B, Hq, L, v.shape[-1]), dtype=np.float64)
     scale = float(np.float64(scale))
     items = [(b, h, r0) for b in range(B) for h in range(Hq) for r0 in range(0, L, row_block)]
+    if bias is not None:
+        bias = np.broadcast_to(np.asarray(bias, dtype=np.float64), (B, Hq, L, S))
 
     def run(item):
         b, h, r0 = item
@@ -158,7 +167,8 @@ def oracle_sdpa(q, k, v, scale, causal_offset: int = NO_CAUSAL, window: int = 0,
         rows = np.arange(r0, min(r0 + row_block, L))
         kv = None if key_mask is None else (key_mask[b] != 0)
         out[b, h, rows] = attention_rows(q[b, h, rows], k[b, hk], v[b, hk], rows, scale,
-                                         causal_offset, window, kv, softcap)
+                                         causal_offset, window, kv, softcap,
+                                         None if bias is None else bias[b, h, rows])
 
     if workers <= 1:
         for it in items:
@@ -170,7 +180,7 @@ def oracle_sdpa(q, k, v, scale, causal_offset: int = NO_CAUSAL, window: int = 0,
 
 
 def oracle_selected_rows(q, k, v, scale, causal_offset, window, key_mask, picks,
-                         softcap: float = 0.0) -> np.ndarray:
+                         softcap: float = 0.0, bias: np.ndarray | None = None) -> np.ndarray:
     """Oracle output for selected (b, h, row) triples only: returns fp64 [len(picks), D].
 
     Used at full workload sizes, where computing every row would take too long."""
@@ -181,8 +191,12 @@ def oracle_selected_rows(q, k, v, scale, causal_offset, window, key_mask, picks,
         kb, vb = _widen(k[b, hk]), _widen(v[b, hk])
         qr = _widen(q[b, h, i:i + 1])
         kv = None if key_mask is None else (key_mask[b] != 0)
+        br = None
+        if bias is not None:
+            bfull = np.broadcast_to(np.asarray(bias, dtype=np.float64), (q.shape[0], Hq, q.shape[2], k.shape[2]))
+            br = bfull[b, h, i:i + 1]
         res.append(attention_rows(qr, kb, vb, np.array([i]), float(np.float64(scale)),
-                                  causal_offset, window, kv, softcap)[0])
+                                  causal_offset, window, kv, softcap, br)[0])
     return np.array(res)
 
 
@@ -201,14 +215,16 @@ def visible_pair_count(B, Hq, L, S, causal_offset, window, key_mask=None, row_bl
 # ----------------------------------------------------------------------------------------------
 # Brute force (pure Python scalars) for tiny cases
 # ----------------------------------------------------------------------------------------------
-def brute_sdpa(q, k, v, scale, causal_offset=NO_CAUSAL, window=0, key_mask=None, softcap=0.0):
+def brute_sdpa(q, k, v, scale, causal_offset=NO_CAUSAL, window=0, key_mask=None, softcap=0.0, bias=None):
     """Scalar-loop SDPA on nested lists / small arrays, with math.exp (and math.tanh for the
-    soft-cap). Shapes as oracle_sdpa."""
+    soft-cap; bias: an array broadcastable to [B, Hq, L, S]). Shapes as oracle_sdpa."""
     q, k, v = _widen(np.asarray(q)), _widen(np.asarray(k)), _widen(np.asarray(v))
     B, Hq, L, D = q.shape
     Hkv, S, Dv = k.shape[1], k.shape[2], v.shape[3]
     G = Hq // Hkv
     out = np.zeros((B, Hq, L, Dv))
+    if bias is not None:
+        bias = np.broadcast_to(np.asarray(bias, dtype=np.float64), (B, Hq, L, S))
     for b in range(B):
         for h in range(Hq):
             hk = h // G
@@ -227,6 +243,10 @@ def brute_sdpa(q, k, v, scale, causal_offset=NO_CAUSAL, window=0, key_mask=None,
                     s = float(scale) * s
                     if softcap > 0.0:
                         s = softcap * math.tanh(s / softcap)
+                    if bias is not None:
+                        s = s + float(bias[b, h, i, j])
+                        if s == -math.inf:
+                            continue
                     keys.append((j, s))
                 if not keys:
                     continue

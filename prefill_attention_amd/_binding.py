@@ -30,7 +30,8 @@ EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_opt", "p
 
 class Options(ctypes.Structure):
     """Mirror of struct pfa_options."""
-    _fields_ = [("flags", ctypes.c_uint), ("softcap", ctypes.c_float)]
+    _fields_ = [("flags", ctypes.c_uint), ("softcap", ctypes.c_float), ("bias", ctypes.c_void_p),
+                ("bias_stride_b", ctypes.c_int64), ("bias_stride_h", ctypes.c_int64), ("bias_stride_l", ctypes.c_int64)]
 
 _lib = None
 
@@ -88,13 +89,14 @@ def version() -> int:
 def prefill_attn_gqa_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: int, Hkv: int, L: int,
                          S: int, D: int, scale: float, causal_offset: int, window: int,
                          key_mask_ptr: int | None, o_ptr: int, stream: int | None,
-                         flags: int = 0, softcap: float = 0.0) -> int:
+                         flags: int = 0, softcap: float = 0.0, bias_ptr: int | None = None,
+                         bias_strides=(0, 0, 0)) -> int:
     """Direct C-ABI call with integer pointers; returns the status code."""
-    if softcap == 0.0:
+    if softcap == 0.0 and not bias_ptr:
         return int(library().prefill_attn_gqa_ex(
             q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
             key_mask_ptr or None, o_ptr, stream or None, flags))
-    opts = Options(flags, softcap)
+    opts = Options(flags, softcap, bias_ptr or None, *bias_strides)
     return int(library().prefill_attn_gqa_opt(
         q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
         key_mask_ptr or None, o_ptr, stream or None, ctypes.byref(opts)))
@@ -102,14 +104,15 @@ def prefill_attn_gqa_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: int, Hk
 
 def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True,
                      causal_offset: int | None = None, window: int = 0, key_mask=None, out=None,
-                     no_skip: bool = False, softcap: float = 0.0, stream=None):
+                     no_skip: bool = False, softcap: float = 0.0, bias=None, stream=None):
     """Grouped-query prefill attention on torch tensors.
 
     q: bf16 [B,Hq,L,D]; k, v: bf16 [B,Hkv,S,D]; key_mask: optional uint8/bool [B,S] (nonzero =
     valid). scale defaults to 1/sqrt(D). With causal=True the causal offset defaults to S - L
     (the chunk is the tail of the S keys); causal=False is bidirectional. window > 0 adds a
-    sliding window of that many keys. softcap > 0 applies logit soft-capping. Returns `out`
-    (allocated if None), bf16 [B,Hq,L,D].
+    sliding window of that many keys. softcap > 0 applies logit soft-capping. bias: optional
+    float32 additive bias broadcastable to [B,Hq,L,S] (last dimension contiguous), added to the
+    scaled scores before the masks. Returns `out` (allocated if None), bf16 [B,Hq,L,D].
     """
     import torch
 
@@ -154,6 +157,19 @@ def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True
         if tuple(key_mask.shape) != (B, S) or key_mask.device != q.device or not key_mask.is_contiguous():
             raise ValueError(f"key_mask must be a contiguous [B,S]=({B},{S}) tensor on {q.device}")
         mask_ptr = key_mask.data_ptr()
+    bias_ptr, bias_strides = None, (0, 0, 0)
+    if bias is not None:
+        if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or bias.device != q.device:
+            raise ValueError(f"bias must be a float32 tensor on {q.device}")
+        while bias.dim() < 4:
+            bias = bias.unsqueeze(0)
+        try:
+            bias = bias.expand(B, Hq, L, S)
+        except RuntimeError as e:
+            raise ValueError(f"bias {tuple(bias.shape)} does not broadcast to [B,Hq,L,S]=({B},{Hq},{L},{S})") from e
+        if bias.stride(3) != 1:
+            raise ValueError("bias must be contiguous along the key dimension")
+        bias_ptr, bias_strides = bias.data_ptr(), (bias.stride(0), bias.stride(1), bias.stride(2))
     if out is None:
         out = torch.empty_like(q)
     elif (out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or out.device != q.device
@@ -165,7 +181,8 @@ def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True
     with torch.cuda.device(q.device):
         rc = prefill_attn_gqa_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
                                   float(scale), int(causal_offset), int(window), mask_ptr,
-                                  out.data_ptr(), stream_ptr, FLAG_NO_SKIP if no_skip else 0, float(softcap))
+                                  out.data_ptr(), stream_ptr, FLAG_NO_SKIP if no_skip else 0, float(softcap),
+                                  bias_ptr, bias_strides)
     if rc != 0:
         raise PfaError(rc, status_str(rc))
     return out
@@ -247,7 +264,7 @@ def prefill_attn_gqa_decode_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: 
         return int(library().prefill_attn_gqa_decode(
             q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
             key_mask_ptr or None, o_ptr, ws_ptr or None, ws_bytes, stream or None))
-    opts = Options(flags, softcap)
+    opts = Options(flags, softcap, None, 0, 0, 0)
     return int(library().prefill_attn_gqa_decode_opt(
         q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
         key_mask_ptr or None, o_ptr, ws_ptr or None, ws_bytes, stream or None, ctypes.byref(opts)))

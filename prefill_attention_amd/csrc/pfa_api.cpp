@@ -78,6 +78,23 @@ int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V, int B, int
                     flags);
   if (rc != PFA_OK) return rc;
   if (!std::isfinite(softcap) || softcap < 0.0f) return PFA_ERR_SCALE;
+  const float* bias = opts ? opts->bias : nullptr;
+  long long bias_nrec = 0;
+  if (bias) {
+    const long long sb = opts->bias_stride_b, sh = opts->bias_stride_h, sl = opts->bias_stride_l;
+    if (key_mask) return PFA_ERR_MASK_ARGS;
+    if (sb < 0 || sh < 0 || sl < 0 || sb > (1LL << 40) || sh > (1LL << 40) || sl > (1LL << 29)) return PFA_ERR_SIZE;
+    const long long block = (static_cast<long long>(L) - 1) * sl + S;  // elements of one (b, h) block
+    if (block >= (1LL << 29)) return PFA_ERR_SIZE;
+    if ((reinterpret_cast<uintptr_t>(bias) & 15u) || (sb & 3) || (sh & 3) || (sl & 3)) return PFA_ERR_ALIGN;
+    bias_nrec = block * 4;
+    const long long last = (static_cast<long long>(B) - 1) * sb + (static_cast<long long>(Hq) - 1) * sh + block;
+    const Range rb{reinterpret_cast<uintptr_t>(bias),
+                   reinterpret_cast<uintptr_t>(bias) + static_cast<uintptr_t>(last) * 4u};
+    const long long q_elems = static_cast<long long>(B) * Hq * L * D;
+    const Range ro{reinterpret_cast<uintptr_t>(O), reinterpret_cast<uintptr_t>(O) + static_cast<uintptr_t>(q_elems) * 2u};
+    if (overlaps(ro, rb)) return PFA_ERR_ALIAS;
+  }
   pfa::Launch p;
   p.q = Q;
   p.k = K;
@@ -98,6 +115,13 @@ int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V, int B, int
   p.flags = flags;
   p.stream = stream;
   p.softcap = softcap;
+  if (bias) {
+    p.bias = bias;
+    p.bias_sb = opts->bias_stride_b;
+    p.bias_sh = opts->bias_stride_h;
+    p.bias_sl = static_cast<int>(opts->bias_stride_l);
+    p.bias_nrec = static_cast<int>(bias_nrec);
+  }
   if (pfa::grid_blocks(p) > INT_MAX) return PFA_ERR_SIZE;
   return pfa::launch_prefill(p);
 }
@@ -286,6 +310,7 @@ int prefill_attn_gqa_decode_opt(const void* Q, const void* K, const void* V, int
   if (rc != PFA_OK) return rc;
   if (flags != 0u) return PFA_ERR_FLAGS;
   if (!std::isfinite(softcap) || softcap < 0.0f) return PFA_ERR_SCALE;
+  if (opts && opts->bias) return PFA_ERR_MASK_ARGS;  // the decode path takes no additive bias
   if (!workspace) return PFA_ERR_NULL;
   if (L > PFA_DECODE_MAX_L || B > (1 << 20) || Hq > (1 << 20)) return PFA_ERR_SIZE;
   const pfa::DecodePlan plan = pfa::decode_plan(B, Hq, Hkv, L, S, D);

@@ -30,6 +30,12 @@ struct Launch {
   int ring = 0;
   // Logit soft-capping (0 = off): each scaled score s becomes softcap * tanh(s / softcap).
   float softcap = 0.0f;
+  // Additive FP32 bias (null = none; dense layout only): element (b, h, i, j) at
+  // bias + b*bias_sb + h*bias_sh + i*bias_sl + j; bias_nrec bytes per (b, h) base are in the call.
+  const float* bias = nullptr;
+  long long bias_sb = 0, bias_sh = 0;
+  int bias_sl = 0;
+  int bias_nrec = 0;
 };
 
 // Query rows handled by one workgroup of the prefill kernel.

@@ -49,6 +49,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -107,6 +108,12 @@ struct Params {
   // position j lives in slot j mod ring.
   int ring;
   float sc_inv, sc_cap_l2;  // soft-capping: scale / cap and cap * log2(e)
+  // Additive FP32 bias (dense layout): element (b, h, i, j) at bias + b*sb + h*sh + i*sl + j;
+  // bias_nrec = bytes from the (b, h) base that belong to the call (reads past it return 0).
+  const float* bias;
+  long long bias_sb, bias_sh;
+  int bias_sl;
+  int bias_nrec;
   int no_skip;
   int batch;
   int n_qblk;
@@ -158,6 +165,11 @@ __device__ __forceinline__ float softcap_l2(float s, float inv, float cap_l2) {
   return __builtin_copysignf(th, y) * cap_l2;
 }
 
+// 16 bytes of an FP32 buffer at byte offset `off` (reads at or past the descriptor's end are 0)
+__device__ __forceinline__ f32x4 buffer_load_f32x4(__amdgpu_buffer_rsrc_t rsrc, unsigned off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+}
+
 __device__ __forceinline__ bool any_zero_byte(uint32_t x) {
   return ((x - 0x01010101u) & ~x & 0x80808080u) != 0u;
 }
@@ -202,12 +214,14 @@ __device__ void key_mask_chunk(const uint8_t* mrow, int S, int t0, int lane, uin
 constexpr int kModeKeyMask = 1;
 constexpr int kModeRing = 2;
 constexpr int kModeSoftcap = 4;
+constexpr int kModeBias = 8;
 
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   constexpr bool KMASK = (MODE & kModeKeyMask) != 0;
   constexpr bool RING = (MODE & kModeRing) != 0;
   constexpr bool SOFTCAP = (MODE & kModeSoftcap) != 0;
+  constexpr bool BIAS = (MODE & kModeBias) != 0;
   using G = Geo<D>;
   constexpr int KQ = G::KQ;
   constexpr int DB = G::DB;
@@ -325,8 +339,39 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   // key), l_run this lane's half of the row sum of P.
   float mref = -INFINITY;
   float l_run = 0.0f;
-  // with soft-capping the scores are turned into the base-2 exponent domain up front
-  const float c = SOFTCAP ? 1.0f : p.c;
+  // with soft-capping or a bias the scores are turned into the base-2 exponent domain up front
+  const float c = (SOFTCAP || BIAS) ? 1.0f : p.c;
+
+  // ---- additive bias: this lane's row of the (b, h) bias, fetched one phase ahead ----
+  // Each wave fetches the 32 bias values of its next softmax tile (8 loads of 4 keys) right before
+  // its MFMA phase, so the loads land while the matrix core works.
+  f32x4 bpre[8];
+  const float* bias_base = nullptr;  // wave-uniform (b, h) base of the bias
+  unsigned bias_row_off = 0;
+  if constexpr (BIAS) {
+    const float* bb = p.bias + (long long)b * p.bias_sb + (long long)h * p.bias_sh;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(bb);
+    const unsigned ahi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32));
+    const unsigned alo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a);
+    bias_base = reinterpret_cast<const float*>(((uintptr_t)ahi << 32) | (uintptr_t)alo);
+    bias_row_off = (unsigned)(qw0 + l32) * (unsigned)p.bias_sl * 4u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bpre[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  auto bias_fetch = [&](int kt) __attribute__((always_inline)) {
+    if constexpr (BIAS) {
+      if (kt < kt_hi) {
+        const __amdgpu_buffer_rsrc_t bias_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(bias_base), 0, p.bias_nrec, kBufferFlags);
+        const unsigned k0 = (unsigned)kt * kBN;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            bpre[4 * kb + j] = buffer_load_f32x4(bias_rsrc, bias_row_off + (k0 + 32 * kb + 8 * j + 4 * hh) * 4u);
+      }
+    }
+  };
 
   // ---- key-mask bitmap (per wave, 64 tiles per chunk) ----
   int mchunk = -1;
@@ -540,6 +585,18 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[kb][v] = softcap_l2(s[kb][v], p.sc_inv, p.sc_cap_l2);
     }
+    if constexpr (BIAS) {
+      // x = c s + log2(e) bias (after the soft-cap, which already is in the base-2 domain), before
+      // the masks (tiny-llm Task 2: the additive mask is applied before the online-softmax update)
+      const float c0 = SOFTCAP ? 1.0f : p.c;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            s[kb][4 * j + i] = __builtin_fmaf(s[kb][4 * j + i], c0, bpre[4 * kb + j][i] * kLog2e);
+    }
     if (tv.need_mask) {
       // Row ii = l32 sees tile keys jj in [lo, lo + span] (causal, window and tail bounds),
       // tested as one unsigned compare per score; span < 0 means the row sees nothing.
@@ -679,6 +736,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     }
     // first half
     if (group_a) {
+      bias_fetch(cur);  // for this iteration's softmax (second half)
       mfma_phase(st_cur, st_prv);
       if (nxt < kt_hi) issue(nxt, st_nxt);  // K of tile nxt
     } else {
@@ -693,6 +751,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
       softmax_phase(tv_cur, st_cur);
       if (nxt < kt_hi) finish(st_nxt);
     } else {
+      bias_fetch(cur);  // for the next iteration's softmax (first half), whose tile is this cur
       mfma_phase(st_cur, st_prv);
       if (nxt < kt_hi) issue(nxt, st_nxt);  // V of tile nxt: first read one iteration later
     }
@@ -756,8 +815,16 @@ int launch_variant(const pfa::Launch& L) {
   const bool sc = L.softcap > 0.0f;
   p.sc_inv = sc ? L.scale / L.softcap : 0.0f;
   p.sc_cap_l2 = sc ? L.softcap * kLog2e : 0.0f;
+  p.bias = L.bias;
+  p.bias_sb = L.bias_sb;
+  p.bias_sh = L.bias_sh;
+  p.bias_sl = L.bias_sl;
+  p.bias_nrec = L.bias_nrec;
   const void* fn;
-  if (L.ring)
+  if (L.bias)
+    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeBias | kModeSoftcap>)
+            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeBias>);
+  else if (L.ring)
     fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeRing | kModeSoftcap>)
             : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeRing>);
   else if (L.key_mask)

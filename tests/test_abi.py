@@ -284,4 +284,37 @@ def test_options_flags_checked(lib):
     assert pfa.prefill_attn_gqa_decode_raw(d["q"], d["k"], d["v"], d["B"], d["Hq"], d["Hkv"], d["L"], d["S"],
                                            d["D"], d["scale"], d["off"], d["window"], d["mask"], d["o"], d["ws"],
                                            need, d["stream"], 0.0, 1) == 9
-    assert ctypes.sizeof(pfa.Options) == 8
+    assert ctypes.sizeof(pfa.Options) == 40
+
+
+BIAS = 13 * A
+
+
+def bcall(bias=BIAS, strides=(0, 0, 48), **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return pfa.prefill_attn_gqa_raw(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["L"], a["S"], a["D"],
+                                    a["scale"], a["off"], a["window"], a["mask"], a["o"], a["stream"], 0, 0.0,
+                                    bias, strides)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=M), 5),                                   # not with a key mask
+    (dict(strides=(0, 0, -4)), 2), (dict(strides=(-4, 0, 48)), 2),
+    (dict(strides=(0, 0, 2 ** 28)), 2),                 # one (b, h) block too large
+    (dict(bias=BIAS + 4), 7), (dict(strides=(0, 0, 50)), 7), (dict(strides=(2, 0, 48)), 7),
+    (dict(bias=O), 8), (dict(bias=O - 64), 8),
+], ids=lambda x: str(x))
+def test_bias_rejected(lib, kw, code):
+    assert bcall(**kw) == code
+
+
+def test_bias_not_on_decode(lib):
+    d = dict(DGOOD)
+    need = pfa.decode_workspace_bytes(d["B"], d["Hq"], d["Hkv"], d["L"], d["S"], d["D"])
+    opts = pfa.Options(0, 0.0, BIAS, 0, 0, 1000)
+    lib_ = pfa.library()
+    rc = lib_.prefill_attn_gqa_decode_opt(d["q"], d["k"], d["v"], d["B"], d["Hq"], d["Hkv"], d["L"], d["S"], d["D"],
+                                          ctypes.c_float(d["scale"]), d["off"], d["window"], None, d["o"], d["ws"],
+                                          need, None, ctypes.byref(opts))
+    assert rc == 5

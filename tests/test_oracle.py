@@ -237,7 +237,40 @@ def pin_softcap():
     for i in range(8):
         assert np.allclose(tiny[0, :, i], v[0, :, : i + 13].mean(axis=1), atol=1e-7, rtol=0)
 
-PINS = [pin_softcap, pin_two_key_sigmoid, pin_rows_sum_to_one, pin_uniform_v_returns_v, pin_window_reductions,
+
+def pin_additive_bias():
+    """Additive bias (tiny-llm Task 2): zero bias is no bias; a -inf bias equals the key mask; a
+    per-row constant cancels (softmax shift invariance); the two-key sigmoid identity on biased
+    scores; scalar brute force with broadcast biases and the causal term."""
+    sig = lambda x: 1.0 / (1.0 + math.exp(-x))
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((2, 2, 6, 8))
+    k = rng.standard_normal((2, 1, 10, 8))
+    v = rng.standard_normal((2, 1, 10, 8))
+    plain = oracle_sdpa(q, k, v, 0.4, causal_offset=4)
+    assert np.array_equal(oracle_sdpa(q, k, v, 0.4, causal_offset=4, bias=np.zeros((6, 10))), plain)
+    km = (rng.random((2, 10)) > 0.4).astype(np.uint8)
+    km[:, 0] = 1
+    neg = np.where(km[:, None, None, :] != 0, 0.0, -np.inf)
+    assert np.allclose(oracle_sdpa(q, k, v, 0.4, causal_offset=4, bias=neg),
+                       oracle_sdpa(q, k, v, 0.4, causal_offset=4, key_mask=km), atol=1e-14, rtol=0)
+    rowc = rng.standard_normal((2, 2, 6, 1)) * 5.0
+    assert np.allclose(oracle_sdpa(q, k, v, 0.4, causal_offset=4, bias=np.broadcast_to(rowc, (2, 2, 6, 10))),
+                       plain, atol=1e-12, rtol=0)
+    q1 = rng.standard_normal((1, 1, 1, 3))
+    k1 = rng.standard_normal((1, 1, 2, 3))
+    v1 = rng.standard_normal((1, 1, 2, 3))
+    bb = np.array([[[[0.7, -1.9]]]])
+    d = 0.5 * float(q1[0, 0, 0] @ k1[0, 0, 1]) - 1.9 - 0.5 * float(q1[0, 0, 0] @ k1[0, 0, 0]) - 0.7
+    ref = v1[0, 0, 0] + sig(d) * (v1[0, 0, 1] - v1[0, 0, 0])
+    assert np.allclose(oracle_sdpa(q1, k1, v1, 0.5, causal_offset=-1, bias=bb)[0, 0, 0], ref, atol=1e-13, rtol=0)
+    for shape in [(6, 10), (2, 1, 6, 10), (1, 2, 1, 10)]:
+        bias = rng.standard_normal(shape) * 2.0
+        got = oracle_sdpa(q, k, v, 0.4, causal_offset=4, window=3, bias=bias, softcap=1.5)
+        ref = brute_sdpa(q, k, v, 0.4, causal_offset=4, window=3, bias=bias, softcap=1.5)
+        assert np.allclose(got, ref, atol=1e-12, rtol=0)
+
+PINS = [pin_softcap, pin_additive_bias, pin_two_key_sigmoid, pin_rows_sum_to_one, pin_uniform_v_returns_v, pin_window_reductions,
         pin_gqa_is_expanded_mha, pin_triu_counts, pin_zero_scale_prefix_means, pin_chunk_equals_tail,
         pin_key_padding, pin_brute_force]
 
@@ -392,17 +425,28 @@ def _bad_key_mask(rows, S, off, W, kv):
 osdpa_visible_orig = osdpa.visible
 
 
-def _bad_scale(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0):
-    return _attention_rows_orig(q_rows, k, v, rows, 1.0, off, W, kv, softcap)
+def _bad_scale(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None):
+    return _attention_rows_orig(q_rows, k, v, rows, 1.0, off, W, kv, softcap, bias_rows)
 
 
-def _bad_softcap_after_mask(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0):
+def _bad_softcap_after_mask(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None):
     # the soft-cap applied after the mask: masked keys (-inf) become -cap, i.e. visible
     S = k.shape[0]
     scores = float(scale) * (q_rows @ k.T) + osdpa.additive_mask(rows, S, off, W, kv)
+    if bias_rows is not None:
+        scores = scores + bias_rows
     if softcap > 0:
         scores = softcap * np.tanh(scores / softcap)
     return osdpa._softmax_rows_times_v(scores, v)
+
+
+def _bad_bias_ignored(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None):
+    return _attention_rows_orig(q_rows, k, v, rows, scale, off, W, kv, softcap, None)
+
+
+def _bad_bias_sign(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None):
+    return _attention_rows_orig(q_rows, k, v, rows, scale, off, W, kv, softcap,
+                                None if bias_rows is None else -bias_rows)
 
 
 def _bad_softcap_unscaled(scores, softcap):
@@ -424,9 +468,12 @@ _attention_rows_orig = osdpa.attention_rows
                                       ("attention_rows", _bad_scale),
                                       ("_softmax_rows_times_v", _bad_empty_rows),
                                       ("attention_rows", _bad_softcap_after_mask),
-                                      ("soft_cap", _bad_softcap_unscaled)],
+                                      ("soft_cap", _bad_softcap_unscaled),
+                                      ("attention_rows", _bad_bias_ignored),
+                                      ("attention_rows", _bad_bias_sign)],
                          ids=["head_map_mod", "causal_plus_one", "window_plus_one", "key_mask_dropped",
-                              "scale_dropped", "empty_rows_nan", "softcap_after_mask", "softcap_unscaled"])
+                              "scale_dropped", "empty_rows_nan", "softcap_after_mask", "softcap_unscaled",
+                              "bias_ignored", "bias_sign"])
 def test_planted_mistake_is_caught(monkeypatch, attr, bad):
     monkeypatch.setattr(osdpa, attr, bad)
     caught = 0

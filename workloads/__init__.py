@@ -48,6 +48,10 @@ CONFIGS: dict[str, dict] = {
     # attn_softcap).
     "long_ctx_32k_softcap50": dict(B=1, Hq=32, Hkv=8, D=128, L=2048, S=32768, causal_offset=30720, window=0,
                                    amp=1.0, key_padding=None, softcap=50.0),
+    # The mid-context chunk with an additive FP32 bias of [L, S] broadcast over batch and heads
+    # (tiny-llm Task 2's broadcastable additive mask), drawn as 2 * N(0, 1) after Q, K, V.
+    "mid_ctx_8k_bias": dict(B=1, Hq=56, Hkv=8, D=128, L=2048, S=8192, causal_offset=6144, window=0,
+                            amp=1.0, key_padding=None, bias="LS"),
     # The sliding-window chunk through the rotating-cache entry point: the first 1023 keys are the
     # cached history (in a 3072-slot ring, key j in slot j mod 3072), the last 2048 the chunk's own
     # keys, appended by the call (TensorFold PR: ring slot of a key row; brotensor kv_cache_append).
@@ -101,9 +105,12 @@ def make_inputs(cfg: dict | str, seed: int = 0, **overrides) -> dict:
         lo, hi = kp
         lengths = rng.integers(lo, hi + 1, size=B)
         key_mask = (np.arange(S)[None, :] < lengths[:, None]).astype(np.uint8)
+    bias = None
+    if c.get("bias") == "LS":
+        bias = (rng.standard_normal((L, S), dtype=np.float32) * np.float32(2.0))
     return dict(
         q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k), v=f32_to_bf16_bits(v),
-        key_mask=key_mask, key_lengths=lengths,
+        key_mask=key_mask, key_lengths=lengths, bias=bias,
         scale=np.float32(1.0 / np.sqrt(np.float32(D))) if c.get("scale") is None else np.float32(c["scale"]),
         B=B, Hq=Hq, Hkv=Hkv, D=D, L=L, S=S,
         causal_offset=int(c.get("causal_offset", NO_CAUSAL)), window=int(c.get("window", 0)),
