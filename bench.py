@@ -170,17 +170,21 @@ def cpu_baseline(workers: int, budget_s: float = 20.0) -> dict:
 
 
 def kernel_name(workload_name: str) -> str:
+    """Name of the dominant kernel as rocprofv3 prints it (prefill MODE bits: 1 key mask, 2 ring,
+    4 soft-cap, 8 bias)."""
     from workloads import CONFIGS, VARLEN_CONFIGS
 
     if workload_name in VARLEN_CONFIGS:
-        return "pfa_prefill_kernel<%d,false,false>" % VARLEN_CONFIGS[workload_name]["D"]
+        return "pfa_prefill_kernel<%d, 0>" % VARLEN_CONFIGS[workload_name]["D"]
     c = CONFIGS[workload_name]
-    if c.get("entry") == "ring":
-        return "pfa_prefill_kernel<%d,false,true> (after pfa_ring_append_kernel)" % c["D"]
     if c.get("entry") == "decode":
-        return "pfa_decode_split_kernel<%d,%d,%s> + pfa_decode_merge_kernel<%d>" % (
-            c["D"], 2 if (c["Hq"] // c["Hkv"]) * c["L"] > 32 else 1, "true" if c["key_padding"] else "false", c["D"])
-    return "pfa_prefill_kernel<%d,%s,false>" % (c["D"], "true" if c["key_padding"] else "false")
+        return "pfa_decode_split_kernel<%d, %d, %s, %s> + pfa_decode_merge_kernel<%d>" % (
+            c["D"], 2 if (c["Hq"] // c["Hkv"]) * c["L"] > 32 else 1, "true" if c["key_padding"] else "false",
+            "true" if c.get("softcap") else "false", c["D"])
+    mode = (1 if c["key_padding"] else 0) | (2 if c.get("entry") == "ring" else 0) | \
+        (4 if c.get("softcap") else 0) | (8 if c.get("bias") else 0)
+    suffix = " (after pfa_ring_append_kernel)" if c.get("entry") == "ring" else ""
+    return "pfa_prefill_kernel<%d, %d>%s" % (c["D"], mode, suffix)
 
 
 def varlen_cpu_baseline(name: str, workers: int, budget_s: float = 20.0) -> dict:

@@ -103,7 +103,7 @@ __device__ __forceinline__ void dma_rows(const void* base, int nrec, lds_char* d
 }
 
 template <int D, int RB, bool KMASK, bool SOFTCAP>
-__global__ __launch_bounds__(64) void pfa_decode_split_kernel(DParams p) {
+__global__ __launch_bounds__(64, (RB == 1 ? 2 : 1)) void pfa_decode_split_kernel(DParams p) {
   using G = DGeo<D>;
   constexpr int KQ = G::KQ;
   constexpr int DB = G::DB;
