@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define PFA_VERSION 10500 /* 1.5.0 */
+#define PFA_VERSION 10600 /* 1.6.0 */
 
 /* causal_offset < 0 selects bidirectional attention (no causal term). */
 #define PFA_NO_CAUSAL (-1)
@@ -66,7 +66,7 @@ enum pfa_status {
   PFA_ERR_SIZE = 2,      /* a size < 1, L or S > PFA_MAX_LEN, or a size product / grid too big  */
   PFA_ERR_GQA = 3,       /* Hq is not a multiple of Hkv                                         */
   PFA_ERR_HEAD_DIM = 4,  /* D is not 64 or 128                                                  */
-  PFA_ERR_MASK_ARGS = 5, /* window > 0 without the causal term                                  */
+  PFA_ERR_MASK_ARGS = 5, /* window > 0 without the causal term; an unsupported mask combination */
   PFA_ERR_SCALE = 6,     /* scale not finite or not > 0; softcap not finite or < 0              */
   PFA_ERR_ALIGN = 7,     /* Q, K, V or O not 16-byte aligned (prefix sums: not 4-byte aligned)  */
   PFA_ERR_ALIAS = 8,     /* O (or the decode workspace) overlaps another buffer of the call     */
@@ -130,12 +130,34 @@ int prefill_attn_gqa_ex(const void* Q, const void* K, const void* V,
  *            pointer and the strides must be multiples of 16 bytes / 4 elements (PFA_ERR_ALIGN);
  *            one (b, h) block, (L - 1) * bias_stride_l + S elements, must stay under 2^29
  *            elements (PFA_ERR_SIZE); it must not overlap O (PFA_ERR_ALIAS).
+ *   sinks    NULL, or DEVICE fp32 [Hq]: one attention-sink logit per query head (mlx-lm
+ *            sliding-window prefill PR, "Correctness", lists attention sinks among the cases; the
+ *            pages give no formula, and the reading taken is the usual one): every row's softmax
+ *            gets one more term, e^sinks[h], in its normaliser, with no value, i.e.
+ *            O[i] = sum_j e^(s_ij) V_j / (sum_j e^(s_ij) + e^sinks[h]) over the visible keys j,
+ *            s_ij the final (scaled, soft-capped, biased) score. The sink is used as given (not
+ *            scaled). Values finite or -inf (-inf = no sink for that head). A row without a
+ *            visible key still gives zeros. Prefill and decode entry points.
+ *   block_sel  NULL, or a DEVICE uint8 block bitmap (TensorFold PR "What changes": MiniMax-M3's
+ *            prompt attention adds a block bitmap, SEL; the pages give no layout, and the reading
+ *            taken is: with query blocks of block_q rows and key blocks of block_k keys, key j is
+ *            visible to row i of (b, h) only if
+ *              block_sel[b * sel_stride_b + h * sel_stride_h + (i / block_q) * sel_stride_q + j / block_k]
+ *            is nonzero, on top of every other mask term). Key blocks whose byte is zero are
+ *            skipped whole (never fetched) unless PFA_FLAG_NO_SKIP is set. block_q must be a
+ *            positive multiple of 32 and block_k of 64 (PFA_ERR_SIZE); strides >= 0 (0
+ *            broadcasts); the bitmap must not overlap O (PFA_ERR_ALIAS). Prefill entry point
+ *            only, and not with a key mask or an additive bias (PFA_ERR_MASK_ARGS).
  */
 typedef struct pfa_options {
   unsigned flags;
   float softcap;
   const float* bias;
   int64_t bias_stride_b, bias_stride_h, bias_stride_l;
+  const float* sinks;
+  const uint8_t* block_sel;
+  int32_t block_q, block_k;
+  int64_t sel_stride_b, sel_stride_h, sel_stride_q;
 } pfa_options;
 
 /* prefill_attn_gqa_ex with options (see pfa_options). */

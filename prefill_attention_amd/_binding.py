@@ -31,7 +31,10 @@ EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_opt", "p
 class Options(ctypes.Structure):
     """Mirror of struct pfa_options."""
     _fields_ = [("flags", ctypes.c_uint), ("softcap", ctypes.c_float), ("bias", ctypes.c_void_p),
-                ("bias_stride_b", ctypes.c_int64), ("bias_stride_h", ctypes.c_int64), ("bias_stride_l", ctypes.c_int64)]
+                ("bias_stride_b", ctypes.c_int64), ("bias_stride_h", ctypes.c_int64), ("bias_stride_l", ctypes.c_int64),
+                ("sinks", ctypes.c_void_p), ("block_sel", ctypes.c_void_p), ("block_q", ctypes.c_int32),
+                ("block_k", ctypes.c_int32), ("sel_stride_b", ctypes.c_int64), ("sel_stride_h", ctypes.c_int64),
+                ("sel_stride_q", ctypes.c_int64)]
 
 _lib = None
 
@@ -90,21 +93,36 @@ def prefill_attn_gqa_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: int, Hk
                          S: int, D: int, scale: float, causal_offset: int, window: int,
                          key_mask_ptr: int | None, o_ptr: int, stream: int | None,
                          flags: int = 0, softcap: float = 0.0, bias_ptr: int | None = None,
-                         bias_strides=(0, 0, 0)) -> int:
+                         bias_strides=(0, 0, 0), sinks_ptr: int | None = None, sel_ptr: int | None = None,
+                         sel_blocks=(0, 0), sel_strides=(0, 0, 0)) -> int:
     """Direct C-ABI call with integer pointers; returns the status code."""
-    if softcap == 0.0 and not bias_ptr:
+    if softcap == 0.0 and not bias_ptr and not sinks_ptr and not sel_ptr:
         return int(library().prefill_attn_gqa_ex(
             q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
             key_mask_ptr or None, o_ptr, stream or None, flags))
-    opts = Options(flags, softcap, bias_ptr or None, *bias_strides)
+    opts = Options(flags, softcap, bias_ptr or None, *bias_strides, sinks_ptr or None, sel_ptr or None,
+                   *sel_blocks, *sel_strides)
     return int(library().prefill_attn_gqa_opt(
         q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
         key_mask_ptr or None, o_ptr, stream or None, ctypes.byref(opts)))
 
 
+def _sinks_ptr(sinks, Hq, device):
+    """Device pointer of a float32 [Hq] sink-logit tensor (None passes through)."""
+    if sinks is None:
+        return None
+    import torch
+
+    if (not isinstance(sinks, torch.Tensor) or sinks.dtype != torch.float32 or tuple(sinks.shape) != (Hq,)
+            or sinks.device != device or not sinks.is_contiguous()):
+        raise ValueError(f"sinks must be a contiguous float32 [Hq]=({Hq},) tensor on {device}")
+    return sinks.data_ptr()
+
+
 def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True,
                      causal_offset: int | None = None, window: int = 0, key_mask=None, out=None,
-                     no_skip: bool = False, softcap: float = 0.0, bias=None, stream=None):
+                     no_skip: bool = False, softcap: float = 0.0, bias=None, sinks=None,
+                     block_sel=None, block_q: int = 0, block_k: int = 0, stream=None):
     """Grouped-query prefill attention on torch tensors.
 
     q: bf16 [B,Hq,L,D]; k, v: bf16 [B,Hkv,S,D]; key_mask: optional uint8/bool [B,S] (nonzero =
@@ -112,7 +130,11 @@ def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True
     (the chunk is the tail of the S keys); causal=False is bidirectional. window > 0 adds a
     sliding window of that many keys. softcap > 0 applies logit soft-capping. bias: optional
     float32 additive bias broadcastable to [B,Hq,L,S] (last dimension contiguous), added to the
-    scaled scores before the masks. Returns `out` (allocated if None), bf16 [B,Hq,L,D].
+    scaled scores before the masks. sinks: optional float32 [Hq] attention-sink logits (one extra
+    softmax term per head, with no value). block_sel: optional uint8/bool block bitmap broadcastable
+    to [B, Hq, ceil(L/block_q), ceil(S/block_k)] (last dimension contiguous); key j is visible to
+    row i only where block_sel[b, h, i // block_q, j // block_k] is nonzero. Returns `out`
+    (allocated if None), bf16 [B,Hq,L,D].
     """
     import torch
 
@@ -170,6 +192,28 @@ def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True
         if bias.stride(3) != 1:
             raise ValueError("bias must be contiguous along the key dimension")
         bias_ptr, bias_strides = bias.data_ptr(), (bias.stride(0), bias.stride(1), bias.stride(2))
+    sinks_ptr = _sinks_ptr(sinks, Hq, q.device)
+    sel_ptr, sel_strides = None, (0, 0, 0)
+    if block_sel is not None:
+        if not isinstance(block_sel, torch.Tensor) or block_sel.device != q.device:
+            raise ValueError(f"block_sel must be a tensor on {q.device}")
+        if block_sel.dtype == torch.bool:
+            block_sel = block_sel.view(torch.uint8)
+        if block_sel.dtype != torch.uint8:
+            raise ValueError("block_sel must be uint8 or bool")
+        if block_q <= 0 or block_k <= 0:
+            raise ValueError("block_sel needs block_q > 0 and block_k > 0")
+        nqb, nkb = -(-L // block_q), -(-S // block_k)
+        while block_sel.dim() < 4:
+            block_sel = block_sel.unsqueeze(0)
+        try:
+            block_sel = block_sel.expand(B, Hq, nqb, nkb)
+        except RuntimeError as e:
+            raise ValueError(f"block_sel {tuple(block_sel.shape)} does not broadcast to "
+                             f"[B,Hq,nqb,nkb]=({B},{Hq},{nqb},{nkb})") from e
+        if nkb > 1 and block_sel.stride(3) != 1:
+            raise ValueError("block_sel must be contiguous along the key-block dimension")
+        sel_ptr, sel_strides = block_sel.data_ptr(), (block_sel.stride(0), block_sel.stride(1), block_sel.stride(2))
     if out is None:
         out = torch.empty_like(q)
     elif (out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or out.device != q.device
@@ -182,7 +226,8 @@ def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True
         rc = prefill_attn_gqa_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
                                   float(scale), int(causal_offset), int(window), mask_ptr,
                                   out.data_ptr(), stream_ptr, FLAG_NO_SKIP if no_skip else 0, float(softcap),
-                                  bias_ptr, bias_strides)
+                                  bias_ptr, bias_strides, sinks_ptr, sel_ptr, (int(block_q), int(block_k)),
+                                  sel_strides)
     if rc != 0:
         raise PfaError(rc, status_str(rc))
     return out
@@ -258,13 +303,14 @@ def decode_workspace_bytes(B: int, Hq: int, Hkv: int, L: int, S: int, D: int) ->
 def prefill_attn_gqa_decode_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: int, Hkv: int, L: int,
                                 S: int, D: int, scale: float, causal_offset: int, window: int,
                                 key_mask_ptr: int | None, o_ptr: int, ws_ptr: int | None, ws_bytes: int,
-                                stream: int | None, softcap: float = 0.0, flags: int = 0) -> int:
+                                stream: int | None, softcap: float = 0.0, flags: int = 0,
+                                sinks_ptr: int | None = None) -> int:
     """Direct C-ABI call of the short-query (decode) entry point; returns the status code."""
-    if softcap == 0.0 and flags == 0:
+    if softcap == 0.0 and flags == 0 and not sinks_ptr:
         return int(library().prefill_attn_gqa_decode(
             q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
             key_mask_ptr or None, o_ptr, ws_ptr or None, ws_bytes, stream or None))
-    opts = Options(flags, softcap, None, 0, 0, 0)
+    opts = Options(flags, softcap, None, 0, 0, 0, sinks_ptr or None)
     return int(library().prefill_attn_gqa_decode_opt(
         q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
         key_mask_ptr or None, o_ptr, ws_ptr or None, ws_bytes, stream or None, ctypes.byref(opts)))
@@ -272,11 +318,12 @@ def prefill_attn_gqa_decode_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: 
 
 def prefill_attn_gqa_decode(q, k, v, *, scale: float | None = None, causal: bool = True,
                             causal_offset: int | None = None, window: int = 0, key_mask=None, out=None,
-                            workspace=None, softcap: float = 0.0, stream=None):
+                            workspace=None, softcap: float = 0.0, sinks=None, stream=None):
     """Short-query (decode, L <= 64) grouped-query attention on torch tensors: the same arguments
     and result as prefill_attn_gqa, computed with the key range split over the chip and a
     deterministic merge. `workspace` is an optional uint8 GPU tensor of at least
-    decode_workspace_bytes(...) bytes (allocated here if None; the library itself never allocates)."""
+    decode_workspace_bytes(...) bytes (allocated here if None; the library itself never allocates).
+    sinks: optional float32 [Hq] attention-sink logits, as in prefill_attn_gqa."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -324,7 +371,7 @@ def prefill_attn_gqa_decode(q, k, v, *, scale: float | None = None, causal: bool
         rc = prefill_attn_gqa_decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
                                          float(scale), int(causal_offset), int(window), mask_ptr,
                                          out.data_ptr(), workspace.data_ptr(), workspace.numel(), stream_ptr,
-                                         float(softcap))
+                                         float(softcap), 0, _sinks_ptr(sinks, Hq, q.device))
     if rc != 0:
         raise PfaError(rc, status_str(rc))
     return out

@@ -65,6 +65,17 @@ int validate(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv
   return PFA_OK;
 }
 
+// Sink logits: fp32 [Hq], 4-byte aligned, not overlapping the output.
+int check_sinks(const pfa_options* opts, int Hq, Range out) {
+  const float* sinks = opts ? opts->sinks : nullptr;
+  if (!sinks) return PFA_OK;
+  if (reinterpret_cast<uintptr_t>(sinks) & 3u) return PFA_ERR_ALIGN;
+  const Range rs{reinterpret_cast<uintptr_t>(sinks),
+                 reinterpret_cast<uintptr_t>(sinks) + static_cast<uintptr_t>(Hq) * 4u};
+  if (overlaps(out, rs)) return PFA_ERR_ALIAS;
+  return PFA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -78,6 +89,10 @@ int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V, int B, int
                     flags);
   if (rc != PFA_OK) return rc;
   if (!std::isfinite(softcap) || softcap < 0.0f) return PFA_ERR_SCALE;
+  const long long q_elems_o = static_cast<long long>(B) * Hq * L * D;
+  const Range ro{reinterpret_cast<uintptr_t>(O), reinterpret_cast<uintptr_t>(O) + static_cast<uintptr_t>(q_elems_o) * 2u};
+  rc = check_sinks(opts, Hq, ro);
+  if (rc != PFA_OK) return rc;
   const float* bias = opts ? opts->bias : nullptr;
   long long bias_nrec = 0;
   if (bias) {
@@ -91,9 +106,23 @@ int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V, int B, int
     const long long last = (static_cast<long long>(B) - 1) * sb + (static_cast<long long>(Hq) - 1) * sh + block;
     const Range rb{reinterpret_cast<uintptr_t>(bias),
                    reinterpret_cast<uintptr_t>(bias) + static_cast<uintptr_t>(last) * 4u};
-    const long long q_elems = static_cast<long long>(B) * Hq * L * D;
-    const Range ro{reinterpret_cast<uintptr_t>(O), reinterpret_cast<uintptr_t>(O) + static_cast<uintptr_t>(q_elems) * 2u};
     if (overlaps(ro, rb)) return PFA_ERR_ALIAS;
+  }
+  const uint8_t* sel = opts ? opts->block_sel : nullptr;
+  if (sel) {
+    if (key_mask || bias) return PFA_ERR_MASK_ARGS;
+    const int bq = opts->block_q, bk = opts->block_k;
+    const long long sb = opts->sel_stride_b, sh = opts->sel_stride_h, sq = opts->sel_stride_q;
+    if (bq < 32 || bq % 32 != 0 || bk < 64 || bk % 64 != 0) return PFA_ERR_SIZE;
+    const long long lim = LLONG_MAX / 4;
+    const long long nqb = (static_cast<long long>(L) + bq - 1) / bq, nkb = (static_cast<long long>(S) + bk - 1) / bk;
+    long long eb, eh, eq;
+    if (sb < 0 || sh < 0 || sq < 0 || !mul_fits(B - 1, sb, lim, &eb) || !mul_fits(Hq - 1, sh, lim, &eh) ||
+        !mul_fits(nqb - 1, sq, lim, &eq))
+      return PFA_ERR_SIZE;
+    const long long last = eb + eh + eq + nkb;  // one past the last byte read
+    const Range rs{reinterpret_cast<uintptr_t>(sel), reinterpret_cast<uintptr_t>(sel) + static_cast<uintptr_t>(last)};
+    if (overlaps(ro, rs)) return PFA_ERR_ALIAS;
   }
   pfa::Launch p;
   p.q = Q;
@@ -121,6 +150,15 @@ int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V, int B, int
     p.bias_sh = opts->bias_stride_h;
     p.bias_sl = static_cast<int>(opts->bias_stride_l);
     p.bias_nrec = static_cast<int>(bias_nrec);
+  }
+  p.sinks = opts ? opts->sinks : nullptr;
+  if (sel) {
+    p.sel = sel;
+    p.sel_bq = opts->block_q;
+    p.sel_bk = opts->block_k;
+    p.sel_sb = opts->sel_stride_b;
+    p.sel_sh = opts->sel_stride_h;
+    p.sel_sq = opts->sel_stride_q;
   }
   if (pfa::grid_blocks(p) > INT_MAX) return PFA_ERR_SIZE;
   return pfa::launch_prefill(p);
@@ -310,7 +348,8 @@ int prefill_attn_gqa_decode_opt(const void* Q, const void* K, const void* V, int
   if (rc != PFA_OK) return rc;
   if (flags != 0u) return PFA_ERR_FLAGS;
   if (!std::isfinite(softcap) || softcap < 0.0f) return PFA_ERR_SCALE;
-  if (opts && opts->bias) return PFA_ERR_MASK_ARGS;  // the decode path takes no additive bias
+  // the decode path takes no additive bias and no block bitmap
+  if (opts && (opts->bias || opts->block_sel)) return PFA_ERR_MASK_ARGS;
   if (!workspace) return PFA_ERR_NULL;
   if (L > PFA_DECODE_MAX_L || B > (1 << 20) || Hq > (1 << 20)) return PFA_ERR_SIZE;
   const pfa::DecodePlan plan = pfa::decode_plan(B, Hq, Hkv, L, S, D);
@@ -328,8 +367,11 @@ int prefill_attn_gqa_decode_opt(const void* Q, const void* K, const void* V, int
   };
   if (overlaps(ws, at(Q, bytes(B, Hq, L, D))) || overlaps(ws, at(K, bytes(B, Hkv, S, D))) ||
       overlaps(ws, at(V, bytes(B, Hkv, S, D))) || overlaps(ws, at(O, bytes(B, Hq, L, D))) ||
-      (key_mask && overlaps(ws, at(key_mask, static_cast<uintptr_t>(B) * static_cast<uintptr_t>(S)))))
+      (key_mask && overlaps(ws, at(key_mask, static_cast<uintptr_t>(B) * static_cast<uintptr_t>(S)))) ||
+      (opts && opts->sinks && overlaps(ws, at(opts->sinks, static_cast<uintptr_t>(Hq) * 4u))))
     return PFA_ERR_ALIAS;
+  rc = check_sinks(opts, Hq, at(O, bytes(B, Hq, L, D)));
+  if (rc != PFA_OK) return rc;
   pfa::Launch p;
   p.q = Q;
   p.k = K;
@@ -350,6 +392,7 @@ int prefill_attn_gqa_decode_opt(const void* Q, const void* K, const void* V, int
   p.flags = 0;
   p.stream = stream;
   p.softcap = softcap;
+  p.sinks = opts ? opts->sinks : nullptr;
   return pfa::launch_decode(p, plan, workspace);
 }
 
@@ -365,10 +408,10 @@ const char* pfa_status_str(int status) {
   switch (status) {
     case PFA_OK: return "ok";
     case PFA_ERR_NULL: return "null pointer (every tensor of the call; varlen prefix sums; the decode workspace)";
-    case PFA_ERR_SIZE: return "invalid size: B, Hq, Hkv, L, S, D must be >= 1 and fit the launch";
+    case PFA_ERR_SIZE: return "invalid size: B, Hq, Hkv, L, S, D must be >= 1 and fit the launch (block bitmap: block_q a multiple of 32, block_k of 64, strides >= 0)";
     case PFA_ERR_GQA: return "Hq must be a multiple of Hkv";
     case PFA_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
-    case PFA_ERR_MASK_ARGS: return "a sliding window (window > 0) requires causal_offset >= 0";
+    case PFA_ERR_MASK_ARGS: return "invalid mask combination: a sliding window (window > 0) requires causal_offset >= 0; a bias or block bitmap takes no key mask, a block bitmap no bias, and the decode path neither";
     case PFA_ERR_SCALE: return "scale must be finite and > 0";
     case PFA_ERR_ALIGN: return "Q, K, V and O must be 16-byte aligned";
     case PFA_ERR_ALIAS: return "O must not overlap Q, K, V or key_mask";

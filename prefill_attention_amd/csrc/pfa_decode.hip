@@ -67,6 +67,7 @@ struct DParams {
   float c;
   int causal, causal_offset, window;
   float sc_inv, sc_cap_l2;  // logit soft-capping: scale / cap and cap * log2(e)
+  const float* sinks;       // null, or fp32 [hq] sink logits (an extra normaliser term per row)
   int n_rowgrp, rows_cap, n_split, tiles_per_split;
   long long n_partials;
 };
@@ -428,7 +429,9 @@ __global__ __launch_bounds__(kMergeThreads) void pfa_decode_merge_kernel(DParams
     __syncthreads();
   }
   if (j == 0) {
-    const float lt = red_l[0];
+    float lt = red_l[0];
+    // an attention sink adds e^sink to the normaliser, relative to the merged maximum
+    if (p.sinks != nullptr && lt > 0.0f) lt += __builtin_amdgcn_exp2f(__builtin_fmaf(p.sinks[h], kLog2e, -mstar));
     const f32x4 at = red[d4];
     uint16_t* orow = o + (((long long)b * p.hq + h) * p.lq + i) * D + 4 * d4;
 #pragma unroll
@@ -460,6 +463,7 @@ int launch_decode_variant(const pfa::Launch& L, const pfa::DecodePlan& plan, voi
   const bool sc = L.softcap > 0.0f;
   p.sc_inv = sc ? L.scale / L.softcap : 0.0f;
   p.sc_cap_l2 = sc ? L.softcap * kLog2e : 0.0f;
+  p.sinks = L.sinks;
   p.n_rowgrp = plan.n_rowgrp;
   p.rows_cap = plan.rows_cap;
   p.n_split = plan.n_split;

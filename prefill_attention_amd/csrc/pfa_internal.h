@@ -36,6 +36,13 @@ struct Launch {
   long long bias_sb = 0, bias_sh = 0;
   int bias_sl = 0;
   int bias_nrec = 0;
+  // Attention sinks (null = none): fp32 [hq] logits, one extra normaliser term e^sink per row.
+  const float* sinks = nullptr;
+  // Block bitmap (null = none; dense layout only): key j visible to row i of (b, h) only if
+  // sel[b*sel_sb + h*sel_sh + (i / sel_bq)*sel_sq + j / sel_bk] != 0; sel_bq % 32 == 0, sel_bk % 64 == 0.
+  const uint8_t* sel = nullptr;
+  int sel_bq = 0, sel_bk = 0;
+  long long sel_sb = 0, sel_sh = 0, sel_sq = 0;
 };
 
 // Query rows handled by one workgroup of the prefill kernel.

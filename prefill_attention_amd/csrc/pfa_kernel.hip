@@ -114,6 +114,14 @@ struct Params {
   long long bias_sb, bias_sh;
   int bias_sl;
   int bias_nrec;
+  // Attention sinks (null = none): fp32 [hq] logits, each an extra normaliser term of its head.
+  const float* sinks;
+  // Block bitmap (dense layout): key j visible to row i of (b, h) only if
+  // sel[b*sel_sb + h*sel_sh + (i / sel_bq)*sel_sq + j / sel_bk] != 0 (sel_bq % 32 == 0,
+  // sel_bk % 64 == 0, so a wave's rows share one query block and a tile's keys one key block).
+  const uint8_t* sel;
+  int sel_bq, sel_bk;
+  long long sel_sb, sel_sh, sel_sq;
   int no_skip;
   int batch;
   int n_qblk;
@@ -210,11 +218,33 @@ __device__ void key_mask_chunk(const uint8_t* mrow, int S, int t0, int lane, uin
   *all = __ballot(al);
 }
 
-// Kernel variants (template MODE bits): a key mask, a rotating cache, logit soft-capping.
+// Per-wave block-bitmap summary for 64 consecutive tiles starting at tile t0: bit i of `any` is
+// set when key block of tile t0+i is selected for some query block in [qb_lo, qb_hi] (the
+// workgroup's rows), bit i of `own` when it is selected for query block qb_own (the wave's rows;
+// -1 for a wave without rows).
+__device__ void sel_chunk(const uint8_t* sel_bh, long long sq, int bk, int qb_lo, int qb_hi, int qb_own,
+                          int n_tiles, int t0, int lane, uint64_t* any, uint64_t* own) {
+  const int t = t0 + lane;
+  bool a = false, o = false;
+  if (t < n_tiles) {
+    const long long kb = (long long)t * kBN / bk;
+    for (int qb = qb_lo; qb <= qb_hi; ++qb) {
+      const bool on = sel_bh[(long long)qb * sq + kb] != 0;
+      a |= on;
+      o |= on & (qb == qb_own);
+    }
+  }
+  *any = __ballot(a);
+  *own = __ballot(o);
+}
+
+// Kernel variants (template MODE bits): a key mask, a rotating cache, logit soft-capping, an
+// additive bias, a block bitmap.
 constexpr int kModeKeyMask = 1;
 constexpr int kModeRing = 2;
 constexpr int kModeSoftcap = 4;
 constexpr int kModeBias = 8;
+constexpr int kModeSel = 16;
 
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
@@ -222,6 +252,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   constexpr bool RING = (MODE & kModeRing) != 0;
   constexpr bool SOFTCAP = (MODE & kModeSoftcap) != 0;
   constexpr bool BIAS = (MODE & kModeBias) != 0;
+  constexpr bool SEL = (MODE & kModeSel) != 0;
   using G = Geo<D>;
   constexpr int KQ = G::KQ;
   constexpr int DB = G::DB;
@@ -373,22 +404,36 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     }
   };
 
-  // ---- key-mask bitmap (per wave, 64 tiles per chunk) ----
+  // ---- key-mask or block-bitmap summary (per wave, 64 tiles per chunk) ----
+  // Key mask: m_any = tiles with a valid key, m_all = tiles whose keys are all valid. Block
+  // bitmap: m_any = tiles some wave of the workgroup selects, m_all = tiles this wave selects.
   int mchunk = -1;
   uint64_t m_any = 0, m_all = 0;
+  const uint8_t* sel_bh = nullptr;
+  int qb_lo = 0, qb_hi = -1, qb_own = -1;
+  if constexpr (SEL) {
+    sel_bh = p.sel + (long long)b * p.sel_sb + (long long)h * p.sel_sh;
+    qb_lo = q0 / p.sel_bq;
+    qb_hi = (q1 - 1) / p.sel_bq;
+    qb_own = wave_active ? qw0 / p.sel_bq : -1;
+  }
   auto ensure_chunk = [&](int kt) __attribute__((always_inline)) {
     const int ch = kt >> 6;
     if (ch != mchunk) {
-      key_mask_chunk(mrow, S, ch << 6, lane, &m_any, &m_all);
+      if constexpr (SEL)
+        sel_chunk(sel_bh, p.sel_sq, p.sel_bk, qb_lo, qb_hi, qb_own, n_tiles, ch << 6, lane, &m_any, &m_all);
+      else
+        key_mask_chunk(mrow, S, ch << 6, lane, &m_any, &m_all);
       mchunk = ch;
     }
   };
-  // Next tile >= k (and < kt_hi) to visit, or kt_hi, packed as (tile << 1) | all_valid. With a
-  // key mask and skipping on, tiles without a valid key are passed over; all_valid tells whether
-  // every key of the returned tile is valid (no elementwise key masking needed).
+  // Next tile >= k (and < kt_hi) to visit, or kt_hi, packed as (tile << 1) | bit. With a key mask
+  // or a block bitmap and skipping on, tiles without a valid (selected) key are passed over. The
+  // bit is m_all's: whether every key of the returned tile is valid (no elementwise key masking
+  // needed), or whether this wave's query block selects the tile.
   auto next_tile = [&](int k) __attribute__((always_inline)) -> int {
     if (k >= kt_hi) return (kt_hi << 1) | 1;
-    if (!kmask) return (k << 1) | 1;
+    if (!kmask && !SEL) return (k << 1) | 1;
     while (k < kt_hi) {
       ensure_chunk(k);
       if (p.no_skip) return (k << 1) | (int)((m_all >> (k & 63)) & 1ull);
@@ -501,15 +546,18 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     const long long t = (long long)causal_offset - W + 1 + qw0;
     return (int)(t < -512 ? -512 : (t > (long long)S + 512 ? (long long)S + 512 : t));
   }();
-  auto view_of = [&](int kt, bool tile_all_valid) __attribute__((always_inline)) -> TileView {
+  auto view_of = [&](int kt, bool tile_bit) __attribute__((always_inline)) -> TileView {
     TileView tv;
     const int key0 = kt * kBN;
-    tv.lim_tail = min(S - key0, kBN);
+    // a tile the wave's query block does not select is a tile without keys (lim_tail = 0)
+    const bool selected = SEL ? tile_bit : true;
+    const bool tile_all_valid = SEL ? true : tile_bit;
+    tv.lim_tail = selected ? min(S - key0, kBN) : 0;
     tv.dc = max(min(cbase - key0, 256), -256);
     tv.dw = max(min(wbase - key0, 256), -256);
     const int lo = max(tv.dw, -ii_last);
     const int hi = min(tv.dc, tv.lim_tail - 1);
-    tv.live = wave_active & ((p.no_skip != 0) | (lo <= hi));
+    tv.live = wave_active & ((p.no_skip != 0) | ((lo <= hi) & selected));
     tv.need_mask = (tv.lim_tail < kBN) | (tv.dc < kBN - 1) | (tv.dw > -31) | !tile_all_valid;
     return tv;
   };
@@ -766,7 +814,10 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
 
   // ---- epilogue: O = acc / l, rows without visible keys -> 0 ----
   if (!wave_active) return;
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  float lt = l_run + __shfl_xor(l_run, 32);
+  // an attention sink adds e^sink to the normaliser, relative to the row's reference maximum
+  // (overflow to +inf gives O = 0, the limit; a -inf sink adds 0)
+  if (p.sinks != nullptr && lt > 0.0f) lt += __builtin_amdgcn_exp2f(__builtin_fmaf(p.sinks[h], kLog2e, -mref));
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   const int row = qw0 + l32;
   if (row >= L) return;
@@ -820,6 +871,13 @@ int launch_variant(const pfa::Launch& L) {
   p.bias_sh = L.bias_sh;
   p.bias_sl = L.bias_sl;
   p.bias_nrec = L.bias_nrec;
+  p.sinks = L.sinks;
+  p.sel = L.sel;
+  p.sel_bq = L.sel_bq;
+  p.sel_bk = L.sel_bk;
+  p.sel_sb = L.sel_sb;
+  p.sel_sh = L.sel_sh;
+  p.sel_sq = L.sel_sq;
   const void* fn;
   if (L.bias)
     fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeBias | kModeSoftcap>)
@@ -830,6 +888,9 @@ int launch_variant(const pfa::Launch& L) {
   else if (L.key_mask)
     fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeKeyMask | kModeSoftcap>)
             : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeKeyMask>);
+  else if (L.sel)
+    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeSel | kModeSoftcap>)
+            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeSel>);
   else
     fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeSoftcap>)
             : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, 0>);

@@ -284,7 +284,28 @@ def test_options_flags_checked(lib):
     assert pfa.prefill_attn_gqa_decode_raw(d["q"], d["k"], d["v"], d["B"], d["Hq"], d["Hkv"], d["L"], d["S"],
                                            d["D"], d["scale"], d["off"], d["window"], d["mask"], d["o"], d["ws"],
                                            need, d["stream"], 0.0, 1) == 9
-    assert ctypes.sizeof(pfa.Options) == 40
+
+
+def test_options_layout_matches_header(tmp_path):
+    """The ctypes mirror of struct pfa_options has the header's size and field offsets (the header
+    compiled by the host C compiler)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = [f[0] for f in pfa.Options._fields_]
+    src = tmp_path / "layout.c"
+    body = "".join(f'  printf("%s %zu\\n", "{f}", offsetof(pfa_options, {f}));\n' for f in fields)
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "pfa.h"\nint main(void) {\n'
+                   '  printf("size %zu\\n", sizeof(pfa_options));\n' + body + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                      text=True).stdout.splitlines())
+    assert int(out["size"]) == ctypes.sizeof(pfa.Options)
+    for f in fields:
+        assert int(out[f]) == getattr(pfa.Options, f).offset, f
 
 
 BIAS = 13 * A
@@ -318,3 +339,43 @@ def test_bias_not_on_decode(lib):
                                           ctypes.c_float(d["scale"]), d["off"], d["window"], None, d["o"], d["ws"],
                                           need, None, ctypes.byref(opts))
     assert rc == 5
+
+
+SINKS = 14 * A
+SEL = 15 * A
+
+
+def ocall(sinks=None, sel=None, blocks=(64, 64), sel_strides=(0, 0, 1), **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return pfa.prefill_attn_gqa_raw(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["L"], a["S"], a["D"],
+                                    a["scale"], a["off"], a["window"], a["mask"], a["o"], a["stream"], 0, 0.0,
+                                    a.get("bias"), a.get("bias_strides", (0, 0, 48)), sinks, sel, blocks,
+                                    sel_strides)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sinks=SINKS + 2), 7),                          # sink logits: 4-byte aligned
+    (dict(sinks=O + 8), 8), (dict(sinks=O - 8), 8),     # and not overlapping O
+    (dict(sel=SEL, blocks=(16, 64)), 2), (dict(sel=SEL, blocks=(48, 64)), 2),   # block_q % 32
+    (dict(sel=SEL, blocks=(32, 32)), 2), (dict(sel=SEL, blocks=(32, 96)), 2),   # block_k % 64
+    (dict(sel=SEL, blocks=(0, 64)), 2), (dict(sel=SEL, sel_strides=(0, -1, 1)), 2),
+    (dict(sel=SEL, sel_strides=(1 << 62, 0, 1), B=2), 2),
+    (dict(sel=SEL, mask=M), 5), (dict(sel=SEL, bias=BIAS), 5),  # not with a key mask or a bias
+    (dict(sel=O), 8), (dict(sel=O - 1, blocks=(32, 64)), 8),  # rows 0-31 and 32: 2 bytes from O - 1
+], ids=lambda x: str(x))
+def test_sinks_and_block_bitmap_rejected(lib, kw, code):
+    assert ocall(**kw) == code
+
+
+def test_block_bitmap_not_on_decode(lib):
+    d = dict(DGOOD)
+    need = pfa.decode_workspace_bytes(d["B"], d["Hq"], d["Hkv"], d["L"], d["S"], d["D"])
+    opts = pfa.Options(0, 0.0, None, 0, 0, 0, None, SEL, 32, 64, 0, 0, 1)
+    rc = pfa.library().prefill_attn_gqa_decode_opt(
+        d["q"], d["k"], d["v"], d["B"], d["Hq"], d["Hkv"], d["L"], d["S"], d["D"], ctypes.c_float(d["scale"]),
+        d["off"], d["window"], None, d["o"], d["ws"], need, None, ctypes.byref(opts))
+    assert rc == 5
+    assert pfa.prefill_attn_gqa_decode_raw(d["q"], d["k"], d["v"], d["B"], d["Hq"], d["Hkv"], d["L"], d["S"],
+                                           d["D"], d["scale"], d["off"], d["window"], None, d["o"], d["ws"],
+                                           need, None, 0.0, 0, O + 2) == 7

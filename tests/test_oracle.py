@@ -270,7 +270,85 @@ def pin_additive_bias():
         ref = brute_sdpa(q, k, v, 0.4, causal_offset=4, window=3, bias=bias, softcap=1.5)
         assert np.allclose(got, ref, atol=1e-12, rtol=0)
 
-PINS = [pin_softcap, pin_additive_bias, pin_two_key_sigmoid, pin_rows_sum_to_one, pin_uniform_v_returns_v, pin_window_reductions,
+
+def pin_sinks():
+    """Attention sinks (one logit per query head, an extra softmax term with no value): a -inf
+    sink is no sink; with all scores 0 and uniform values c, a row with n visible keys gives
+    c n / (n + e^sink) (per query head, not per KV head); one visible key of score s gives
+    V sigmoid(s - sink) (the sink is not scaled); a row without visible keys stays 0; adding a
+    constant to every score and to the sinks changes nothing; scalar brute force."""
+    sig = lambda x: 1.0 / (1.0 + math.exp(-x))
+    rng = np.random.default_rng(29)
+    q = rng.standard_normal((2, 4, 6, 8))
+    k = rng.standard_normal((2, 2, 10, 8))
+    v = rng.standard_normal((2, 2, 10, 8))
+    plain = oracle_sdpa(q, k, v, 0.4, causal_offset=4)
+    assert np.array_equal(oracle_sdpa(q, k, v, 0.4, causal_offset=4, sinks=np.full(4, -np.inf)), plain)
+    sinks = np.array([-1.0, 0.5, 2.0, math.log(3.0)])
+    c = rng.standard_normal((2, 2, 1, 8))
+    o = oracle_sdpa(q, np.zeros_like(k), np.broadcast_to(c, v.shape), 0.4, causal_offset=4, sinks=sinks)
+    for h in range(4):
+        for i in range(6):
+            n = i + 4 + 1
+            assert np.allclose(o[:, h, i], c[:, h // 2, 0] * n / (n + math.exp(sinks[h])), atol=1e-14, rtol=0)
+    q1 = rng.standard_normal((1, 1, 1, 3))
+    k1 = rng.standard_normal((1, 1, 1, 3))
+    v1 = rng.standard_normal((1, 1, 1, 3))
+    s1 = 0.5 * float(q1[0, 0, 0] @ k1[0, 0, 0])
+    got = oracle_sdpa(q1, k1, v1, 0.5, causal_offset=0, sinks=np.array([1.25]))[0, 0, 0]
+    assert np.allclose(got, v1[0, 0, 0] * sig(s1 - 1.25), atol=1e-14, rtol=0)
+    km = np.ones((2, 10), dtype=np.uint8)
+    km[1, :] = 0
+    o = oracle_sdpa(q, k, v, 0.4, key_mask=km, sinks=sinks)
+    assert np.all(o[1] == 0.0) and np.all(np.isfinite(o))
+    shifted = oracle_sdpa(q, k, v, 0.4, causal_offset=4, sinks=sinks + 3.5, bias=np.full((6, 10), 3.5))
+    assert np.allclose(shifted, oracle_sdpa(q, k, v, 0.4, causal_offset=4, sinks=sinks), atol=1e-13, rtol=0)
+    bias = rng.standard_normal((1, 4, 6, 10))
+    got = oracle_sdpa(q, k, v, 0.4, causal_offset=4, window=3, softcap=1.5, bias=bias, sinks=sinks)
+    ref = brute_sdpa(q, k, v, 0.4, causal_offset=4, window=3, softcap=1.5, bias=bias, sinks=sinks)
+    assert np.allclose(got, ref, atol=1e-12, rtol=0)
+
+
+def pin_block_bitmap():
+    """Block bitmap: an all-ones bitmap is no bitmap; a block-diagonal bitmap without the causal
+    term is independent attention inside each block; the bitmap equals the -inf additive bias of
+    its element-wise expansion (built with a Kronecker product); K = 0 with a ramp in V gives the
+    mean visible key index, worked by hand; scalar brute force with per-head bitmaps, the causal
+    term and a window."""
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((2, 4, 12, 8))
+    k = rng.standard_normal((2, 2, 12, 8))
+    v = rng.standard_normal((2, 2, 12, 8))
+    plain = oracle_sdpa(q, k, v, 0.4, causal_offset=0)
+    ones = np.ones((1, 1, 3, 3), dtype=np.uint8)
+    assert np.array_equal(oracle_sdpa(q, k, v, 0.4, causal_offset=0, block_sel=ones, block_q=4, block_k=4), plain)
+    diag = np.eye(3, dtype=np.uint8)[None, None]
+    o = oracle_sdpa(q, k, v, 0.4, block_sel=diag, block_q=4, block_k=4)
+    for r in range(3):
+        sl = slice(4 * r, 4 * r + 4)
+        assert np.allclose(o[:, :, sl], oracle_sdpa(q[:, :, sl], k[:, :, sl], v[:, :, sl], 0.4), atol=1e-13, rtol=0)
+    L, S, bq, bk = 12, 12, 4, 6
+    sel = (rng.random((2, 4, 3, 2)) > 0.4).astype(np.uint8)
+    dense = np.kron(sel, np.ones((bq, bk), dtype=np.uint8))[..., :L, :S]
+    neg = np.where(dense != 0, 0.0, -np.inf)
+    got = oracle_sdpa(q, k, v, 0.4, causal_offset=0, block_sel=sel, block_q=bq, block_k=bk)
+    ref = oracle_sdpa(q, k, v, 0.4, causal_offset=0, bias=neg)
+    assert np.allclose(got, ref, atol=1e-14, rtol=0)
+    # L = 4 rows, S = 8 keys, blocks of 2 rows x 4 keys, bitmap [[1, 0], [0, 1]], no causal term:
+    # rows 0-1 see keys 0-3 (mean index 1.5), rows 2-3 see keys 4-7 (mean index 5.5)
+    vr = np.zeros((1, 1, 8, 2))
+    vr[0, 0, :, 0] = np.arange(8)
+    o = oracle_sdpa(rng.standard_normal((1, 1, 4, 2)), np.zeros((1, 1, 8, 2)), vr, 1.0,
+                    block_sel=np.array([[[[1, 0], [0, 1]]]]), block_q=2, block_k=4)
+    assert np.allclose(o[0, 0, :, 0], [1.5, 1.5, 5.5, 5.5], atol=1e-14, rtol=0)
+    kk = rng.standard_normal((2, 2, 11, 8))
+    vv = rng.standard_normal((2, 2, 11, 8))
+    sel = (rng.random((2, 4, 2, 4)) > 0.5).astype(np.uint8)
+    got = oracle_sdpa(q[:, :, :7], kk, vv, 0.4, causal_offset=4, window=5, block_sel=sel, block_q=4, block_k=3)
+    ref = brute_sdpa(q[:, :, :7], kk, vv, 0.4, causal_offset=4, window=5, block_sel=sel, block_q=4, block_k=3)
+    assert np.allclose(got, ref, atol=1e-12, rtol=0)
+
+PINS = [pin_sinks, pin_block_bitmap, pin_softcap, pin_additive_bias, pin_two_key_sigmoid, pin_rows_sum_to_one, pin_uniform_v_returns_v, pin_window_reductions,
         pin_gqa_is_expanded_mha, pin_triu_counts, pin_zero_scale_prefix_means, pin_chunk_equals_tail,
         pin_key_padding, pin_brute_force]
 
@@ -425,11 +503,11 @@ def _bad_key_mask(rows, S, off, W, kv):
 osdpa_visible_orig = osdpa.visible
 
 
-def _bad_scale(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None):
-    return _attention_rows_orig(q_rows, k, v, rows, 1.0, off, W, kv, softcap, bias_rows)
+def _bad_scale(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None, sink=None, sel_rows=None):
+    return _attention_rows_orig(q_rows, k, v, rows, 1.0, off, W, kv, softcap, bias_rows, sink, sel_rows)
 
 
-def _bad_softcap_after_mask(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None):
+def _bad_softcap_after_mask(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None, sink=None, sel_rows=None):
     # the soft-cap applied after the mask: masked keys (-inf) become -cap, i.e. visible
     S = k.shape[0]
     scores = float(scale) * (q_rows @ k.T) + osdpa.additive_mask(rows, S, off, W, kv)
@@ -437,16 +515,18 @@ def _bad_softcap_after_mask(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, 
         scores = scores + bias_rows
     if softcap > 0:
         scores = softcap * np.tanh(scores / softcap)
-    return osdpa._softmax_rows_times_v(scores, v)
+    if sel_rows is not None:
+        scores = np.where(sel_rows, scores, -np.inf)
+    return osdpa._softmax_rows_times_v(scores, v, sink)
 
 
-def _bad_bias_ignored(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None):
-    return _attention_rows_orig(q_rows, k, v, rows, scale, off, W, kv, softcap, None)
+def _bad_bias_ignored(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None, sink=None, sel_rows=None):
+    return _attention_rows_orig(q_rows, k, v, rows, scale, off, W, kv, softcap, None, sink, sel_rows)
 
 
-def _bad_bias_sign(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None):
+def _bad_bias_sign(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None, sink=None, sel_rows=None):
     return _attention_rows_orig(q_rows, k, v, rows, scale, off, W, kv, softcap,
-                                None if bias_rows is None else -bias_rows)
+                                None if bias_rows is None else -bias_rows, sink, sel_rows)
 
 
 def _bad_softcap_unscaled(scores, softcap):
@@ -454,7 +534,44 @@ def _bad_softcap_unscaled(scores, softcap):
     return softcap * np.tanh(scores) if softcap > 0 else scores
 
 
-def _bad_empty_rows(scores, v):
+def _bad_sink_ignored(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None, sink=None, sel_rows=None):
+    return _attention_rows_orig(q_rows, k, v, rows, scale, off, W, kv, softcap, bias_rows, None, sel_rows)
+
+
+def _bad_sink_scaled(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None, sink=None, sel_rows=None):
+    return _attention_rows_orig(q_rows, k, v, rows, scale, off, W, kv, softcap, bias_rows,
+                                None if sink is None else sink * scale, sel_rows)
+
+
+def _bad_sink_sign(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None, sink=None, sel_rows=None):
+    return _attention_rows_orig(q_rows, k, v, rows, scale, off, W, kv, softcap, bias_rows,
+                                None if sink is None else -sink, sel_rows)
+
+
+def _bad_sel_ignored(q_rows, k, v, rows, scale, off, W, kv, softcap=0.0, bias_rows=None, sink=None, sel_rows=None):
+    return _attention_rows_orig(q_rows, k, v, rows, scale, off, W, kv, softcap, bias_rows, sink, None)
+
+
+def _bad_sel_swapped_blocks(rows, S, sel_bh, block_q, block_k):
+    # block sizes exchanged (indices clamped into the bitmap, so the mistake gives values, not errors)
+    sel_bh = np.asarray(sel_bh)
+    qb = np.minimum(np.asarray(rows, dtype=np.int64) // int(block_k), sel_bh.shape[0] - 1)
+    kb = np.minimum(np.arange(S, dtype=np.int64) // int(block_q), sel_bh.shape[1] - 1)
+    return sel_bh[qb][:, kb] != 0
+
+
+def _bad_sel_transposed(rows, S, sel_bh, block_q, block_k):
+    qb = np.asarray(rows, dtype=np.int64) // int(block_q)
+    kb = np.arange(S, dtype=np.int64) // int(block_k)
+    # bitmap read as [key block, query block] (indices clamped into it)
+    t = np.asarray(sel_bh)
+    return t[np.minimum(kb, t.shape[0] - 1)][:, np.minimum(qb, t.shape[1] - 1)].T != 0
+
+
+_block_selected_orig = osdpa.block_selected
+
+
+def _bad_empty_rows(scores, v, sink=None):
     m = np.max(scores, axis=1, keepdims=True)
     p = np.exp(scores - m)
     return (p @ v) / np.sum(p, axis=1, keepdims=True)
@@ -470,10 +587,17 @@ _attention_rows_orig = osdpa.attention_rows
                                       ("attention_rows", _bad_softcap_after_mask),
                                       ("soft_cap", _bad_softcap_unscaled),
                                       ("attention_rows", _bad_bias_ignored),
-                                      ("attention_rows", _bad_bias_sign)],
+                                      ("attention_rows", _bad_bias_sign),
+                                      ("attention_rows", _bad_sink_ignored),
+                                      ("attention_rows", _bad_sink_scaled),
+                                      ("attention_rows", _bad_sink_sign),
+                                      ("attention_rows", _bad_sel_ignored),
+                                      ("block_selected", _bad_sel_swapped_blocks),
+                                      ("block_selected", _bad_sel_transposed)],
                          ids=["head_map_mod", "causal_plus_one", "window_plus_one", "key_mask_dropped",
                               "scale_dropped", "empty_rows_nan", "softcap_after_mask", "softcap_unscaled",
-                              "bias_ignored", "bias_sign"])
+                              "bias_ignored", "bias_sign", "sink_ignored", "sink_scaled", "sink_sign",
+                              "sel_ignored", "sel_swapped_blocks", "sel_transposed"])
 def test_planted_mistake_is_caught(monkeypatch, attr, bad):
     monkeypatch.setattr(osdpa, attr, bad)
     caught = 0
