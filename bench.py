@@ -49,6 +49,8 @@ WORKLOADS = {
     "decode_l1_32k": ["decode_l1_32k"],
     "decode_l8_8k": ["decode_l8_8k"],
     "decode_b8_l1_4k": ["decode_b8_l1_4k"],
+    "long_ctx_32k_sinks": ["long_ctx_32k_sinks"],
+    "long_ctx_32k_sel": ["long_ctx_32k_sel"],
 }
 DESCRIPTION = {
     "causal_8k_32k": "causal GQA prefill chunks, L=2048 on S=8192 (Hq=56,Hkv=8) and on S=32768 "
@@ -71,6 +73,27 @@ def visible_pairs(c: dict, key_lengths=None) -> int:
         lo = max(0, i + off - W + 1) if W > 0 else 0
         total += max(0, hi - lo + 1)
     return B * Hq * total
+
+
+def sel_visible_pairs(c: dict, block_sel, block_q: int, block_k: int) -> int:
+    """Visible (row, key) cells over all query heads under a causal mask and a block bitmap
+    [Hq, n_qblocks, n_kblocks]: per row, the causal key range [0, i + off] intersected with the
+    selected key blocks, counted block by block."""
+    import numpy as np
+
+    L, S, off = c["L"], c["S"], c["causal_offset"]
+    i = np.arange(L, dtype=np.int64)
+    hi = np.minimum(S - 1, i + off) if off >= 0 else np.full(L, S - 1, dtype=np.int64)  # last visible key
+    nkb = block_sel.shape[2]
+    kb0 = np.arange(nkb, dtype=np.int64) * block_k
+    # keys of block kb visible to row i: clamp(hi_i + 1 - kb0, 0, min(block_k, S - kb0))
+    width = np.minimum(block_k, S - kb0)
+    per = np.clip(hi[:, None] + 1 - kb0[None, :], 0, width[None, :])  # [L, nkb]
+    qb = i // block_q
+    total = 0
+    for h in range(block_sel.shape[0]):
+        total += int((per * block_sel[h][qb]).sum())
+    return c["B"] * total
 
 
 def varlen_visible_pairs(x: dict) -> int:
@@ -171,7 +194,7 @@ def cpu_baseline(workers: int, budget_s: float = 20.0) -> dict:
 
 def kernel_name(workload_name: str) -> str:
     """Name of the dominant kernel as rocprofv3 prints it (prefill MODE bits: 1 key mask, 2 ring,
-    4 soft-cap, 8 bias)."""
+    4 soft-cap, 8 bias, 16 block bitmap)."""
     from workloads import CONFIGS, VARLEN_CONFIGS
 
     if workload_name in VARLEN_CONFIGS:
@@ -182,7 +205,7 @@ def kernel_name(workload_name: str) -> str:
             c["D"], 2 if (c["Hq"] // c["Hkv"]) * c["L"] > 32 else 1, "true" if c["key_padding"] else "false",
             "true" if c.get("softcap") else "false", c["D"])
     mode = (1 if c["key_padding"] else 0) | (2 if c.get("entry") == "ring" else 0) | \
-        (4 if c.get("softcap") else 0) | (8 if c.get("bias") else 0)
+        (4 if c.get("softcap") else 0) | (8 if c.get("bias") else 0) | (16 if c.get("block_sel") else 0)
     suffix = " (after pfa_ring_append_kernel)" if c.get("entry") == "ring" else ""
     return "pfa_prefill_kernel<%d, %d>%s" % (c["D"], mode, suffix)
 
@@ -291,10 +314,17 @@ def main() -> int:
             kw["softcap"] = float(c["softcap"])
         if x.get("bias") is not None:
             kw["bias"] = torch.from_numpy(x["bias"]).to(dev)
+        if x.get("sinks") is not None:
+            kw["sinks"] = torch.from_numpy(x["sinks"]).to(dev)
+        if x.get("block_sel") is not None:
+            kw.update(block_sel=torch.from_numpy(x["block_sel"]).to(dev), block_q=x["block_q"], block_k=x["block_k"])
         if c.get("entry") == "decode":
             kw["workspace"] = torch.empty(pfa.decode_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["S"], c["D"]),
                                           dtype=torch.uint8, device=dev)
-        flops = 4 * c["D"] * visible_pairs(c, x["key_lengths"])
+        if x.get("block_sel") is not None:
+            flops = 4 * c["D"] * sel_visible_pairs(c, x["block_sel"], x["block_q"], x["block_k"])
+        else:
+            flops = 4 * c["D"] * visible_pairs(c, x["key_lengths"])
         total_flops += flops
 
         fn = pfa.prefill_attn_gqa_decode if c.get("entry") == "decode" else pfa.prefill_attn_gqa

@@ -36,6 +36,7 @@
 //  * Workgroups are ordered so that those sharing a KV head land on the same XCD (the hardware
 //    deals workgroups to the 8 XCDs round-robin), heaviest causal blocks first.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "../../include/pfa.h"
@@ -570,7 +571,9 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   // a wave with no scores to make runs GEMM1 for nothing, and a wave with no probabilities runs
   // GEMM2 on pb = 0, which adds exact zeros to the accumulator (it starts at +0 and sums
   // non-negative weights, so it is never -0 and acc + 0 == acc bit for bit).
-  auto mfma_phase = [&](int st1, int st2) __attribute__((always_inline)) {
+  auto mfma_run = [&](int st1, int st2, auto do_g1, auto do_g2) __attribute__((always_inline)) {
+    constexpr bool DO1 = decltype(do_g1)::value;
+    constexpr bool DO2 = decltype(do_g2)::value;
     const lds_char* base1 = (const lds_char*)lds_raw + st1 * G::kStageBytes;
     const lds_char* base2 = (const lds_char*)lds_raw + st2 * G::kStageBytes;
     auto load_g1 = [&](int j) __attribute__((always_inline)) -> bf16x8 {
@@ -602,24 +605,41 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[2 * kb + c2], acc[db], 0, 0, 0);
     };
     bf16x8 ring[kRing];
-    constexpr int NS = NG1 + NG2;  // alternate: even steps GEMM1, odd steps GEMM2
+    // both: even steps GEMM1, odd steps GEMM2 (NG1 == NG2); otherwise the one GEMM alone
+    constexpr int NS = (DO1 ? NG1 : 0) + (DO2 ? NG2 : 0);
+    auto is_g2 = [](int m) { return DO1 && DO2 ? (m & 1) != 0 : DO2; };
+    auto index = [](int m) { return DO1 && DO2 ? (m >> 1) : m; };
 #pragma unroll
     for (int m = 0; m < NS + kRing - 1; ++m) {
       if (m < NS) {
-        if (m & 1) {
-          ring[m % kRing] = load_g2(m >> 1);
+        if (is_g2(m)) {
+          ring[m % kRing] = load_g2(index(m));
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
         } else {
-          ring[m % kRing] = load_g1(m >> 1);
+          ring[m % kRing] = load_g1(index(m));
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         }
       }
       const int u = m - (kRing - 1);
       if (u >= 0) {
-        if (u & 1) mma_g2(u >> 1, ring[u % kRing]);
-        else mma_g1(u >> 1, ring[u % kRing]);
+        if (is_g2(u)) mma_g2(index(u), ring[u % kRing]);
+        else mma_g1(index(u), ring[u % kRing]);
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       }
+    }
+  };
+  // With a block bitmap a wave often has no keys in the tile (its query block did not select
+  // it) while the workgroup visits it for the other waves: then its GEMM1 (scores never used)
+  // and its GEMM2 of a tile without keys (P = 0, adding exact zeros) are left out.
+  auto mfma_phase = [&](int st1, int st2, bool live1, bool live2) __attribute__((always_inline)) {
+    using T = std::true_type;
+    using F = std::false_type;
+    if constexpr (SEL) {
+      if (live1 && live2) mfma_run(st1, st2, T{}, T{});
+      else if (live1) mfma_run(st1, st2, T{}, F{});
+      else if (live2) mfma_run(st1, st2, F{}, T{});
+    } else {
+      mfma_run(st1, st2, T{}, T{});
     }
   };
 
@@ -785,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     // first half
     if (group_a) {
       bias_fetch(cur);  // for this iteration's softmax (second half)
-      mfma_phase(st_cur, st_prv);
+      mfma_phase(st_cur, st_prv, tv_cur.live, tv_prv.live);
       if (nxt < kt_hi) issue(nxt, st_nxt);  // K of tile nxt
     } else {
       softmax_phase(tv_prv, st_prv);
@@ -800,7 +820,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
       if (nxt < kt_hi) finish(st_nxt);
     } else {
       bias_fetch(cur);  // for the next iteration's softmax (first half), whose tile is this cur
-      mfma_phase(st_cur, st_prv);
+      mfma_phase(st_cur, st_prv, tv_cur.live, tv_prv.live);
       if (nxt < kt_hi) issue(nxt, st_nxt);  // V of tile nxt: first read one iteration later
     }
     lds_barrier();

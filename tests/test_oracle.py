@@ -608,3 +608,23 @@ def test_planted_mistake_is_caught(monkeypatch, attr, bad):
             except AssertionError:
                 caught += 1
     assert caught >= 1, f"no pin caught the planted mistake in {attr}"
+
+
+def test_generator_variant_draws():
+    """Sinks and the block bitmap are drawn after Q, K, V: the value stream of Q, K, V is that of the
+    plain workload; the bitmap keeps key block 0 and the block of each query block's last causal
+    key, and selects about `density` of the rest."""
+    plain = make_inputs("long_ctx_32k", seed=0, L=256, S=4096, causal_offset=3840, Hq=4, Hkv=1, D=8)
+    for name in ("long_ctx_32k_sinks", "long_ctx_32k_sel"):
+        x = make_inputs(name, seed=0, L=256, S=4096, causal_offset=3840, Hq=4, Hkv=1, D=8)
+        for key in ("q", "k", "v"):
+            assert np.array_equal(x[key], plain[key])
+    s = make_inputs("long_ctx_32k_sinks", seed=0)
+    assert s["sinks"].shape == (32,) and s["sinks"].dtype == np.float32
+    x = make_inputs("long_ctx_32k_sel", seed=0)
+    sel, bq, bk = x["block_sel"], x["block_q"], x["block_k"]
+    assert sel.shape == (32, 16, 64) and (bq, bk) == (128, 512)
+    assert np.all(sel[:, :, 0] == 1)
+    for qb in range(16):
+        assert np.all(sel[:, qb, (qb * 128 + 127 + 30720) // 512] == 1)
+    assert 0.2 < sel.mean() < 0.35

@@ -14,6 +14,12 @@ Workload recipe (shapes from the pages' workloads, values synthetic):
 * ``scale`` is the float32 value of ``1/sqrt(D)``, handed to both sides unchanged.
 * Key padding: ``key_mask[b, j] = 1`` for ``j < n_b`` with ``n_b`` drawn uniformly from the
   integers 1024..4096 inclusive.
+* Additive bias ``[L, S]``: ``2 * N(0, 1)`` float32, drawn after Q, K, V.
+* Attention sinks ``[Hq]``: ``N(0, 1)`` float32 logits, drawn after Q, K, V (and the bias).
+* Block bitmap ``[Hq, ceil(L/block_q), ceil(S/block_k)]`` (uint8, broadcast over the batch): the
+  key block holding the query block's last causal key and key block 0 are always selected, every
+  other key block with probability ``density`` (uniform draws after Q, K, V, bias and sinks) --
+  a selection that keeps the local block and a few distant ones, as block-sparse prefill does.
 """
 from __future__ import annotations
 
@@ -65,6 +71,14 @@ CONFIGS: dict[str, dict] = {
                          amp=1.0, key_padding=None, entry="decode"),
     "decode_b8_l1_4k": dict(B=8, Hq=32, Hkv=8, D=128, L=1, S=4096, causal_offset=4095, window=0,
                             amp=1.0, key_padding=None, entry="decode"),
+    # The long-context chunk with one attention-sink logit per query head (mlx-lm sliding-window
+    # prefill PR: attention sinks among the cases its prefill path reproduces).
+    "long_ctx_32k_sinks": dict(B=1, Hq=32, Hkv=8, D=128, L=2048, S=32768, causal_offset=30720, window=0,
+                               amp=1.0, key_padding=None, sinks=True),
+    # The long-context chunk under a block bitmap (TensorFold PR: MiniMax-M3's block bitmap SEL):
+    # query blocks of 128 rows select 512-key blocks, about a quarter of the causal blocks.
+    "long_ctx_32k_sel": dict(B=1, Hq=32, Hkv=8, D=128, L=2048, S=32768, causal_offset=30720, window=0,
+                             amp=1.0, key_padding=None, block_sel=dict(block_q=128, block_k=512, density=0.25)),
 }
 
 
@@ -108,9 +122,23 @@ def make_inputs(cfg: dict | str, seed: int = 0, **overrides) -> dict:
     bias = None
     if c.get("bias") == "LS":
         bias = (rng.standard_normal((L, S), dtype=np.float32) * np.float32(2.0))
+    sinks = rng.standard_normal(Hq, dtype=np.float32) if c.get("sinks") else None
+    block_sel = None
+    bs = c.get("block_sel")
+    if bs is not None:
+        bq, bk = int(bs["block_q"]), int(bs["block_k"])
+        nqb, nkb = -(-L // bq), -(-S // bk)
+        block_sel = (rng.random((Hq, nqb, nkb)) < float(bs["density"])).astype(np.uint8)
+        block_sel[:, :, 0] = 1
+        off = int(c.get("causal_offset", NO_CAUSAL))
+        if off >= 0:
+            for qb in range(nqb):
+                last = min(S - 1, min(L, (qb + 1) * bq) - 1 + off)
+                block_sel[:, qb, last // bk] = 1
     return dict(
         q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k), v=f32_to_bf16_bits(v),
-        key_mask=key_mask, key_lengths=lengths, bias=bias,
+        key_mask=key_mask, key_lengths=lengths, bias=bias, sinks=sinks, block_sel=block_sel,
+        block_q=int(bs["block_q"]) if bs else 0, block_k=int(bs["block_k"]) if bs else 0,
         scale=np.float32(1.0 / np.sqrt(np.float32(D))) if c.get("scale") is None else np.float32(c["scale"]),
         B=B, Hq=Hq, Hkv=Hkv, D=D, L=L, S=S,
         causal_offset=int(c.get("causal_offset", NO_CAUSAL)), window=int(c.get("window", 0)),
