@@ -254,6 +254,10 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   constexpr bool SOFTCAP = (MODE & kModeSoftcap) != 0;
   constexpr bool BIAS = (MODE & kModeBias) != 0;
   constexpr bool SEL = (MODE & kModeSel) != 0;
+  // Plain scores (no soft-cap, no bias): Q is pre-scaled by scale * log2(e) and each tile's score
+  // accumulator starts at minus the row's reference maximum, so the MFMA result is already the
+  // exponent of exp2 (no per-score multiply-add in the softmax).
+  constexpr bool PRESCALED = !SOFTCAP && !BIAS;
   using G = Geo<D>;
   constexpr int KQ = G::KQ;
   constexpr int DB = G::DB;
@@ -351,8 +355,14 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     if (row < L) {
       const uint16_t* qrow = p.q + q_base + (long long)row * q_stride;
 #pragma unroll
-      for (int kk = 0; kk < KQ; ++kk)
+      for (int kk = 0; kk < KQ; ++kk) {
         qreg[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * hh);
+        if constexpr (PRESCALED) {
+          // q * scale * log2(e), rounded to bf16 (RNE) once per workgroup
+#pragma unroll
+          for (int t = 0; t < 8; ++t) qreg[kk][t] = (__bf16)((float)qreg[kk][t] * p.c);
+        }
+      }
     } else {
 #pragma unroll
       for (int kk = 0; kk < KQ; ++kk)
@@ -371,8 +381,14 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   // key), l_run this lane's half of the row sum of P.
   float mref = -INFINITY;
   float l_run = 0.0f;
-  // with soft-capping or a bias the scores are turned into the base-2 exponent domain up front
-  const float c = (SOFTCAP || BIAS) ? 1.0f : p.c;
+  // start value of a tile's pre-scaled score accumulator: -mref in every element (0 while the
+  // row has no reference), rewritten only when the reference is raised
+  f32x16 s_init;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) s_init[v] = 0.0f;
+  // with soft-capping or a bias the scores are turned into the base-2 exponent domain up front;
+  // pre-scaled scores come out of the MFMA in that domain
+  const float c = (SOFTCAP || BIAS || PRESCALED) ? 1.0f : p.c;
 
   // ---- additive bias: this lane's row of the (b, h) bias, fetched one phase ahead ----
   // Each wave fetches the 32 bias values of its next softmax tile (8 loads of 4 keys) right before
@@ -595,7 +611,8 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
         f32x16 z;
 #pragma unroll
         for (int v = 0; v < 16; ++v) z[v] = 0.0f;
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], z, 0, 0, 0);
+        // pre-scaled scores start from minus the row's reference (kept in s_init)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], PRESCALED ? s_init : z, 0, 0, 0);
       } else {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s[kb], 0, 0, 0);
       }
@@ -712,7 +729,10 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     const float t2b = max3(t1[3], t1[4], t1[5]);
     const float t2c = max3(t1[6], t1[7], t1[8]);
     const float t2d = max3(t1[9], t1[10], t1[11]);
-    const float mx = max_with_partner_half(max3(t2a, t2b, max2(t2c, t2d))) * c;
+    // pre-scaled scores are relative to the reference the tile's GEMM1 started from
+    const float msub_old = (mref == -INFINITY) ? 0.0f : mref;
+    const float mx = PRESCALED ? max_with_partner_half(max3(t2a, t2b, max2(t2c, t2d))) + msub_old
+                               : max_with_partner_half(max3(t2a, t2b, max2(t2c, t2d))) * c;
     // Lazy rescaling: the reference is raised (and the accumulators rescaled) only when some
     // row's tile maximum exceeds it by more than 2^8 in probability, or a row meets its first
     // visible key (mx - mref = +inf); otherwise P <= 256, exact arithmetic on both sides of the
@@ -721,27 +741,8 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     const bool raise = __any((mx - mref) > kLazyLog2);
     const float mnew = raise ? max2(mref, mx) : mref;
     const float msub_new = (mnew == -INFINITY) ? 0.0f : mnew;
-    // P in bf16 pairs; the row sum is taken over the rounded values (the weights that multiply
-    // V), one dot product with (1, 1) per pair in four independent chains. The operand is
-    // assembled from whole 32-bit pairs: extracting pairs back out of the bf16x8 vector is
-    // mis-lowered by the compiler.
-    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      u32x4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(r[8 * q4 + 2 * i], c, -msub_new));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(r[8 * q4 + 2 * i + 1], c, -msub_new));
-        const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
-        ls[i] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, ls[i], false);
-        w[i] = __builtin_bit_cast(unsigned, pr);
-      }
-      pb[q4] = __builtin_bit_cast(bf16x8, w);
-    }
-    const float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     if (raise) {
-      // the accumulator gets this tile's P.V next; rescale it to the raised reference first
+      // rescale the accumulator and the sum to the raised reference before this tile's terms
       // (a row still without keys keeps alpha = 1: its accumulator and sum are zero)
       const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref - mnew);
 #pragma unroll
@@ -749,9 +750,40 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
       l_run *= alpha;
+      if constexpr (PRESCALED) {
+        // the tile's scores were taken against the old reference: shift them (in the MFMA result
+        // registers, which the path without a raise leaves as they are)
+        const float delta = msub_new - msub_old;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[kb][v] -= delta;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s_init[v] = -msub_new;
+      }
     }
     mref = mnew;
-    l_run += lsum;
+    // P in bf16 pairs; the row sum is taken over the rounded values (the weights that multiply
+    // V), one dot product with (1, 1) per pair in four independent chains, the first seeded with
+    // the running sum. The operand is assembled from whole 32-bit pairs: extracting pairs back
+    // out of the bf16x8 vector is mis-lowered by the compiler.
+    float ls[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = s[q4 >> 1][8 * (q4 & 1) + 2 * i], x1 = s[q4 >> 1][8 * (q4 & 1) + 2 * i + 1];
+        const float e0 = PRESCALED ? __builtin_amdgcn_exp2f(x0) : __builtin_amdgcn_exp2f(__builtin_fmaf(x0, c, -msub_new));
+        const float e1 = PRESCALED ? __builtin_amdgcn_exp2f(x1) : __builtin_amdgcn_exp2f(__builtin_fmaf(x1, c, -msub_new));
+        const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+        const float seed = q4 > 0 ? ls[i] : (i == 0 ? l_run : 0.0f);
+        ls[i] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, seed, false);
+        w[i] = __builtin_bit_cast(unsigned, pr);
+      }
+      pb[q4] = __builtin_bit_cast(bf16x8, w);
+    }
+    l_run = (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
 
   // ---- main loop ----
@@ -783,7 +815,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   tv_prv.live = false;
   int st_cur = 0, st_prv = kStages - 1;
   auto softmax_phase = [&](const TileView& tv, int st) __attribute__((always_inline)) {
-    if (tv.live) {
+    if (__builtin_amdgcn_readfirstlane((int)tv.live)) {  // wave-uniform: a scalar branch
       softmax(tv, st);
     } else {
 #pragma unroll
