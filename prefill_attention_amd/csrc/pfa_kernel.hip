@@ -824,44 +824,72 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
         for (int t = 0; t < 8; ++t) pb[i][t] = (__bf16)0.0f;
     }
   };
-  while (cur < kt_hi || prv < kt_hi) {
-    const int packed_nxt = next_tile(cur + 1 <= kt_hi ? cur + 1 : kt_hi);
-    const int nxt = packed_nxt >> 1;
-    const bool all_nxt = packed_nxt & 1;
-    const int st_nxt = st_cur + 1 == kStages ? 0 : st_cur + 1;
-    if (cur < kt_hi) {
-      tv_cur = view_of(cur, all_cur);
-    } else {
-      tv_cur.live = false;
+  // `group` is the wave's group: a runtime flag (one loop for both groups, their phases selected
+  // under the execution mask) or, with a bias, a constant (the two groups run separate copies of
+  // the loop behind a branch on a wave-uniform value, so the compiler sees each group's own tile
+  // fetches only and does not make one group's LDS reads wait for the loads of the other: its
+  // bias loads. Without a bias the shared loop is the faster one.)
+  auto main_loop = [&](auto group) __attribute__((always_inline)) {
+    const bool GA = group;
+    bool first_iter = true;  // tile cur of the first iteration was fetched whole by the prologue
+    while (cur < kt_hi || prv < kt_hi) {
+      const int packed_nxt = next_tile(cur + 1 <= kt_hi ? cur + 1 : kt_hi);
+      const int nxt = packed_nxt >> 1;
+      const bool all_nxt = packed_nxt & 1;
+      const int st_nxt = st_cur + 1 == kStages ? 0 : st_cur + 1;
+      if (cur < kt_hi) {
+        tv_cur = view_of(cur, all_cur);
+      } else {
+        tv_cur.live = false;
+      }
+      // first half
+      if (GA) {
+        bias_fetch(cur);  // for this iteration's softmax (second half)
+        mfma_phase(st_cur, st_prv, tv_cur.live, tv_prv.live);
+        if (nxt < kt_hi) issue(nxt, st_nxt);  // K of tile nxt
+      } else {
+        // With a bias, V of tile cur is fetched here rather than at the end of the previous
+        // iteration: no tile fetch is then in flight across the loop edge, so the MFMA phase's
+        // LDS reads need not wait for the bias loads issued just before it.
+        if constexpr (BIAS) {
+          if (!first_iter && cur < kt_hi) issue(cur, st_cur);
+        }
+        softmax_phase(tv_prv, st_prv);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // V of tile cur has landed
+      }
+      // Nothing stored to LDS in the first half is read in the second (the K in flight targets
+      // the stage nobody reads this iteration), so the middle barrier only aligns the phases.
+      __builtin_amdgcn_s_barrier();
+      // second half
+      if (GA) {
+        softmax_phase(tv_cur, st_cur);
+        if (nxt < kt_hi) finish(st_nxt);
+        // with a bias, also wait where no fetch was issued, so that no path leaves one in flight
+        if constexpr (BIAS) __builtin_amdgcn_s_waitcnt(0x0F70);
+      } else {
+        bias_fetch(cur);  // for the next iteration's softmax (first half), whose tile is this cur
+        mfma_phase(st_cur, st_prv, tv_cur.live, tv_prv.live);
+        if constexpr (!BIAS) {
+          if (nxt < kt_hi) issue(nxt, st_nxt);  // V of tile nxt: first read one iteration later
+        }
+      }
+      lds_barrier();
+      if constexpr (BIAS) first_iter = false;
+      prv = cur;
+      tv_prv = tv_cur;
+      st_prv = st_cur;
+      cur = nxt;
+      all_cur = all_nxt;
+      st_cur = st_nxt;
     }
-    // first half
-    if (group_a) {
-      bias_fetch(cur);  // for this iteration's softmax (second half)
-      mfma_phase(st_cur, st_prv, tv_cur.live, tv_prv.live);
-      if (nxt < kt_hi) issue(nxt, st_nxt);  // K of tile nxt
-    } else {
-      softmax_phase(tv_prv, st_prv);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // V of tile cur (fetched last iteration) has landed
-    }
-    // Nothing stored to LDS in the first half is read in the second (the K in flight targets the
-    // stage nobody reads this iteration), so the middle barrier only aligns the phases.
-    __builtin_amdgcn_s_barrier();
-    // second half
-    if (group_a) {
-      softmax_phase(tv_cur, st_cur);
-      if (nxt < kt_hi) finish(st_nxt);
-    } else {
-      bias_fetch(cur);  // for the next iteration's softmax (first half), whose tile is this cur
-      mfma_phase(st_cur, st_prv, tv_cur.live, tv_prv.live);
-      if (nxt < kt_hi) issue(nxt, st_nxt);  // V of tile nxt: first read one iteration later
-    }
-    lds_barrier();
-    prv = cur;
-    tv_prv = tv_cur;
-    st_prv = st_cur;
-    cur = nxt;
-    all_cur = all_nxt;
-    st_cur = st_nxt;
+  };
+  if constexpr (BIAS) {
+    if (__builtin_amdgcn_readfirstlane(wave) < 4)
+      main_loop(std::true_type{});
+    else
+      main_loop(std::false_type{});
+  } else {
+    main_loop(group_a);
   }
 
   // ---- epilogue: O = acc / l, rows without visible keys -> 0 ----
