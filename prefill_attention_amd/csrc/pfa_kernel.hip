@@ -254,10 +254,6 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   constexpr bool SOFTCAP = (MODE & kModeSoftcap) != 0;
   constexpr bool BIAS = (MODE & kModeBias) != 0;
   constexpr bool SEL = (MODE & kModeSel) != 0;
-  // Plain scores (no soft-cap, no bias): Q is pre-scaled by scale * log2(e) and each tile's score
-  // accumulator starts at minus the row's reference maximum, so the MFMA result is already the
-  // exponent of exp2 (no per-score multiply-add in the softmax).
-  constexpr bool PRESCALED = !SOFTCAP && !BIAS;
   using G = Geo<D>;
   constexpr int KQ = G::KQ;
   constexpr int DB = G::DB;
@@ -355,14 +351,8 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     if (row < L) {
       const uint16_t* qrow = p.q + q_base + (long long)row * q_stride;
 #pragma unroll
-      for (int kk = 0; kk < KQ; ++kk) {
+      for (int kk = 0; kk < KQ; ++kk)
         qreg[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * hh);
-        if constexpr (PRESCALED) {
-          // q * scale * log2(e), rounded to bf16 (RNE) once per workgroup
-#pragma unroll
-          for (int t = 0; t < 8; ++t) qreg[kk][t] = (__bf16)((float)qreg[kk][t] * p.c);
-        }
-      }
     } else {
 #pragma unroll
       for (int kk = 0; kk < KQ; ++kk)
@@ -381,14 +371,8 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   // key), l_run this lane's half of the row sum of P.
   float mref = -INFINITY;
   float l_run = 0.0f;
-  // start value of a tile's pre-scaled score accumulator: -mref in every element (0 while the
-  // row has no reference), rewritten only when the reference is raised
-  f32x16 s_init;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) s_init[v] = 0.0f;
-  // with soft-capping or a bias the scores are turned into the base-2 exponent domain up front;
-  // pre-scaled scores come out of the MFMA in that domain
-  const float c = (SOFTCAP || BIAS || PRESCALED) ? 1.0f : p.c;
+  // with soft-capping or a bias the scores are turned into the base-2 exponent domain up front
+  const float c = (SOFTCAP || BIAS) ? 1.0f : p.c;
 
   // ---- additive bias: this lane's row of the (b, h) bias, fetched one phase ahead ----
   // Each wave fetches the 32 bias values of its next softmax tile (8 loads of 4 keys) right before
@@ -611,8 +595,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
         f32x16 z;
 #pragma unroll
         for (int v = 0; v < 16; ++v) z[v] = 0.0f;
-        // pre-scaled scores start from minus the row's reference (kept in s_init)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], PRESCALED ? s_init : z, 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], z, 0, 0, 0);
       } else {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s[kb], 0, 0, 0);
       }
@@ -682,7 +665,8 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
           for (int i = 0; i < 4; ++i)
             s[kb][4 * j + i] = __builtin_fmaf(s[kb][4 * j + i], c0, bpre[4 * kb + j][i] * kLog2e);
     }
-    if (tv.need_mask) {
+    // masked scores become -inf (run on tiles that cross an edge)
+    auto apply_mask = [&]() __attribute__((always_inline)) {
       // Row ii = l32 sees tile keys jj in [lo, lo + span] (causal, window and tail bounds),
       // tested as one unsigned compare per score; span < 0 means the row sees nothing.
       const int ii = l32;
@@ -710,7 +694,8 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
           }
         }
       }
-    }
+    };
+    if (tv.need_mask) apply_mask();
     // per lane: one query row, 32 of the tile's 64 keys. Short dependency chains: a tree of
     // 3-input maxima, the cross-half exchange as a VALU lane swap, independent exponentials and
     // four partial sums.
@@ -729,10 +714,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     const float t2b = max3(t1[3], t1[4], t1[5]);
     const float t2c = max3(t1[6], t1[7], t1[8]);
     const float t2d = max3(t1[9], t1[10], t1[11]);
-    // pre-scaled scores are relative to the reference the tile's GEMM1 started from
-    const float msub_old = (mref == -INFINITY) ? 0.0f : mref;
-    const float mx = PRESCALED ? max_with_partner_half(max3(t2a, t2b, max2(t2c, t2d))) + msub_old
-                               : max_with_partner_half(max3(t2a, t2b, max2(t2c, t2d))) * c;
+    const float mx = max_with_partner_half(max3(t2a, t2b, max2(t2c, t2d))) * c;
     // Lazy rescaling: the reference is raised (and the accumulators rescaled) only when some
     // row's tile maximum exceeds it by more than 2^8 in probability, or a row meets its first
     // visible key (mx - mref = +inf); otherwise P <= 256, exact arithmetic on both sides of the
@@ -750,17 +732,6 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
       l_run *= alpha;
-      if constexpr (PRESCALED) {
-        // the tile's scores were taken against the old reference: shift them (in the MFMA result
-        // registers, which the path without a raise leaves as they are)
-        const float delta = msub_new - msub_old;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) s[kb][v] -= delta;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s_init[v] = -msub_new;
-      }
     }
     mref = mnew;
     // P in bf16 pairs; the row sum is taken over the rounded values (the weights that multiply
@@ -773,9 +744,8 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
       u32x4 w;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x0 = s[q4 >> 1][8 * (q4 & 1) + 2 * i], x1 = s[q4 >> 1][8 * (q4 & 1) + 2 * i + 1];
-        const float e0 = PRESCALED ? __builtin_amdgcn_exp2f(x0) : __builtin_amdgcn_exp2f(__builtin_fmaf(x0, c, -msub_new));
-        const float e1 = PRESCALED ? __builtin_amdgcn_exp2f(x1) : __builtin_amdgcn_exp2f(__builtin_fmaf(x1, c, -msub_new));
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(r[8 * q4 + 2 * i], c, -msub_new));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(r[8 * q4 + 2 * i + 1], c, -msub_new));
         const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
         const float seed = q4 > 0 ? ls[i] : (i == 0 ? l_run : 0.0f);
         ls[i] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, seed, false);
