@@ -254,6 +254,11 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   constexpr bool SOFTCAP = (MODE & kModeSoftcap) != 0;
   constexpr bool BIAS = (MODE & kModeBias) != 0;
   constexpr bool SEL = (MODE & kModeSel) != 0;
+  // Soft-cap without a bias: the row maximum is taken on the raw scores (the cap is increasing),
+  // and each score's exponent is cap log2(e) tanh(y) - reference with y = scale * s / cap, as
+  // (cap_l2 - reference) - 2 cap_l2 / (1 + 2^z), z = 2 log2(e) y, all in FP32: one FMA folds the
+  // reference in and no sign handling is needed.
+  constexpr bool CAPFAST = SOFTCAP && !BIAS;
   using G = Geo<D>;
   constexpr int KQ = G::KQ;
   constexpr int DB = G::DB;
@@ -645,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
 
   // ---- the VALU phase: mask, online softmax, P in bf16, accumulator rescale ----
   auto softmax = [&](const TileView& tv, int st) __attribute__((always_inline)) {
-    if constexpr (SOFTCAP) {
+    if constexpr (SOFTCAP && !CAPFAST) {
       // logit soft-capping before the masks and the softmax (brotensor flash_attention_decode,
       // attn_softcap): x = log2(e) * cap * tanh(scale * s / cap)
 #pragma unroll
@@ -714,7 +719,19 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     const float t2b = max3(t1[3], t1[4], t1[5]);
     const float t2c = max3(t1[6], t1[7], t1[8]);
     const float t2d = max3(t1[9], t1[10], t1[11]);
-    const float mx = max_with_partner_half(max3(t2a, t2b, max2(t2c, t2d))) * c;
+    const float mtile = max_with_partner_half(max3(t2a, t2b, max2(t2c, t2d)));
+    // z = 2 log2(e) scale s / cap (soft-cap only)
+    const float zk = CAPFAST ? 2.0f * kLog2e * p.sc_inv : 0.0f;
+    float mx;
+    if constexpr (CAPFAST) {
+      // the tile maximum of the capped exponents, from the largest raw score (-inf: none seen)
+      mx = (mtile == -INFINITY)
+               ? -INFINITY
+               : __builtin_fmaf(__builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(mtile * zk)), -2.0f * p.sc_cap_l2,
+                                p.sc_cap_l2);
+    } else {
+      mx = mtile * c;
+    }
     // Lazy rescaling: the reference is raised (and the accumulators rescaled) only when some
     // row's tile maximum exceeds it by more than 2^8 in probability, or a row meets its first
     // visible key (mx - mref = +inf); otherwise P <= 256, exact arithmetic on both sides of the
@@ -734,6 +751,20 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
       l_run *= alpha;
     }
     mref = mnew;
+    if constexpr (CAPFAST) {
+      const float k0 = p.sc_cap_l2 - msub_new;
+#pragma unroll
+      for (int v = 0; v < 32; ++v)
+        r[v] = __builtin_fmaf(__builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(r[v] * zk)), -2.0f * p.sc_cap_l2, k0);
+      if (tv.need_mask) {
+        // a masked score caps to a finite value: mask the exponents themselves
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          r[v] = (s[0][v] == -INFINITY) ? -INFINITY : r[v];
+          r[16 + v] = (s[1][v] == -INFINITY) ? -INFINITY : r[16 + v];
+        }
+      }
+    }
     // P in bf16 pairs; the row sum is taken over the rounded values (the weights that multiply
     // V), one dot product with (1, 1) per pair in four independent chains, the first seeded with
     // the running sum. The operand is assembled from whole 32-bit pairs: extracting pairs back
@@ -744,8 +775,10 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
       u32x4 w;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(r[8 * q4 + 2 * i], c, -msub_new));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(r[8 * q4 + 2 * i + 1], c, -msub_new));
+        const float e0 = CAPFAST ? __builtin_amdgcn_exp2f(r[8 * q4 + 2 * i])
+                                 : __builtin_amdgcn_exp2f(__builtin_fmaf(r[8 * q4 + 2 * i], c, -msub_new));
+        const float e1 = CAPFAST ? __builtin_amdgcn_exp2f(r[8 * q4 + 2 * i + 1])
+                                 : __builtin_amdgcn_exp2f(__builtin_fmaf(r[8 * q4 + 2 * i + 1], c, -msub_new));
         const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
         const float seed = q4 > 0 ? ls[i] : (i == 0 ? l_run : 0.0f);
         ls[i] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, seed, false);
