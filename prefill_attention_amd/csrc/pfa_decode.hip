@@ -369,11 +369,238 @@ __global__ __launch_bounds__(64, (RB == 1 ? 2 : 1)) void pfa_decode_split_kernel
   }
 }
 
+// Decode-split kernel for at most 32 rows per KV head and no key mask (one-token decode and short
+// chunks of small groups): K goes from memory straight into the registers of the GEMM1 operand
+// (lane l: key l % 32, 16 bytes of dimensions per MFMA step, read by buffer loads whose descriptor
+// ends at the last key), only V is staged in LDS (three 32-key stages, for the transpose reads),
+// and while tile t is used tiles t+1 and t+2 are in flight: twice the bytes in flight per
+// workgroup of the kernel above, in a quarter of its LDS. Same partials and arithmetic per tile.
+template <int D, bool SOFTCAP>
+__global__ __launch_bounds__(64, 2) void pfa_decode_kreg_kernel(DParams p) {
+  using G = DGeo<D>;
+  constexpr int KQ = G::KQ;
+  constexpr int DB = G::DB;
+  constexpr int kPerTile = KQ + G::kDmaPerTile;  // memory instructions per tile (K loads, V DMA)
+  __shared__ __attribute__((aligned(1024))) char lds_raw[3 * G::kTileBytes];
+
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // ---- workgroup -> (b, kv head, split): one row group (rows_cap <= 32) ----
+  long long id = blockIdx.x;
+  const int split = (int)(id % p.n_split);
+  id /= p.n_split;
+  const int hk = (int)(id % p.hkv);
+  const int b = (int)(id / p.hkv);
+  const long long part = blockIdx.x;
+  const int L = p.lq, S = p.sk;
+  const int R = p.group * L;
+
+  // ---- this lane's row and its visible key interval [lo, hi] ----
+  bf16x8 qreg[KQ];
+  int lo = S, hi = -1;  // empty
+  if (l32 < R) {
+    const int g = l32 / L, i = l32 % L;
+    const uint16_t* qrow = p.q + (((long long)b * p.hq + hk * p.group + g) * L + i) * (long long)D;
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * hh);
+    lo = 0;
+    hi = S - 1;
+    if (p.causal) {
+      const long long pos = (long long)i + p.causal_offset;
+      hi = (int)(pos < hi ? pos : hi);
+      if (p.window > 0) {
+        const long long w0 = pos - p.window + 1;
+        lo = (int)(w0 > 0 ? w0 : 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) qreg[kk][t] = (__bf16)0.0f;
+  }
+  int grp_lo = lo <= hi ? lo : S, grp_hi = lo <= hi ? hi : -1;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    grp_lo = min(grp_lo, __shfl_xor(grp_lo, o));
+    grp_hi = max(grp_hi, __shfl_xor(grp_hi, o));
+  }
+  const int n_tiles = (S + kTk - 1) / kTk;
+  int t_begin = split * p.tiles_per_split;
+  int t_end = min(t_begin + p.tiles_per_split, n_tiles);
+  if (grp_hi < grp_lo) {
+    t_end = t_begin;
+  } else {
+    t_begin = max(t_begin, grp_lo / kTk);
+    t_end = min(t_end, grp_hi / kTk + 1);
+  }
+  const uint16_t* kg = p.k + ((long long)b * p.hkv + hk) * (long long)S * D;
+  const uint16_t* vg = p.v + ((long long)b * p.hkv + hk) * (long long)S * D;
+
+  // DMA instruction j of a V tile: lane offset off_v0 + 1024 j (row j * kRowsPerDma + lane / CPR;
+  // the swizzle of those rows does not depend on j)
+  unsigned off_v0;
+  {
+    const int row = lane / G::kChunksPerRow;
+    const int pch = lane % G::kChunksPerRow;
+    off_v0 = (unsigned)(row * G::kRowBytes + 16 * (pch ^ G::swz_v(row)));
+  }
+  const unsigned off_k = (unsigned)(l32 * G::kRowBytes + 16 * hh);  // + 32 kk
+  auto uniform_ptr = [&](const void* ptr) __attribute__((always_inline)) -> const void* {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(ptr);
+    const unsigned ahi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32));
+    const unsigned alo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a);
+    return reinterpret_cast<const void*>(((uintptr_t)ahi << 32) | (uintptr_t)alo);
+  };
+  bf16x8 kreg[3][KQ];
+  // K of tile t into kreg[buf], V of tile t into `stage`; keys past S, and every key of a tile at
+  // or past t_end (the padding steps below), read as zeros
+  auto issue = [&](int t, bf16x8* kr, char* stage) __attribute__((always_inline)) {
+    const long long key0 = (long long)t * kTk;
+    long long rows = t < t_end ? (long long)S - key0 : 0;
+    rows = rows < 0 ? 0 : (rows > kTk ? kTk : rows);
+    const int nrec = __builtin_amdgcn_readfirstlane((int)rows * G::kRowBytes);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_ptr(kg + key0 * D)), 0, nrec, kBufferFlags);
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk)
+      kr[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off_k + 32 * kk, 0, 0));
+    unsigned off_v[G::kDmaPerTile];
+#pragma unroll
+    for (int j = 0; j < G::kDmaPerTile; ++j) off_v[j] = off_v0 + 1024u * j;
+    dma_rows<G::kDmaPerTile>(uniform_ptr(vg + key0 * D), nrec, (lds_char*)stage, off_v);
+  };
+  int a_v;
+  {
+    const int g16 = lane >> 4, loc = lane & 15, r4 = loc >> 2, cc = loc & 3;
+    const int row = 4 * (g16 >> 1) + r4;
+    a_v = row * G::kRowBytes + 64 * (G::swz_v(row) >> 2) + 32 * (g16 & 1) + 8 * cc;
+  }
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[db][v] = 0.0f;
+  float m = -INFINITY, l = 0.0f;
+  const float c = SOFTCAP ? 1.0f : p.c;
+  // the row's keys within this split: [lo, min(hi, last key of tile t_end - 1)]
+  const int hi_split = min(hi, t_end * kTk - 1);
+  const bool empty = hi_split < lo;
+  const unsigned span = empty ? 0u : (unsigned)(hi_split - lo);
+  const int lo_eff = empty ? S + kTk : lo;
+
+  // One step on tile t (K in kr, V in `cur`): wait for it (the next tile may stay in flight), the
+  // scores, then tile t+2 to the buffers tile t-1 used (`nxt2`, kr2), softmax and P.V. The stages
+  // are restrict pointers: the fetch into `nxt2` is never read in the step, so the compiler keeps
+  // it in flight across the step's LDS reads.
+  auto step = [&](int t, const bf16x8* kr, bf16x8* kr2, char* __restrict__ cur, char* __restrict__ nxt2)
+                  __attribute__((always_inline)) {
+    // vmcnt(kPerTile): only tile t+1's instructions may still be outstanding
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (kPerTile & 15) | ((kPerTile >> 4) << 14));
+    const lds_char* base = (const lds_char*)cur;
+    f32x16 s;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[kk], qreg[kk], s, 0, 0, 0);
+    // tile t+2 goes out once this tile's K registers have been read
+    issue(t + 2, kr2, nxt2);
+    if constexpr (SOFTCAP) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = softcap_l2(s[v], p.sc_inv, p.sc_cap_l2);
+    }
+    const int key0 = t * kTk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = key0 + 8 * j + 4 * hh + i;
+        s[4 * j + i] = ((unsigned)(key - lo_eff) <= span) ? s[4 * j + i] : -INFINITY;
+      }
+    unsigned pw[8];
+    {
+      float mx = s[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = max2(mx, s[v]);
+      mx = max_with_partner_half(mx) * c;
+      const float mnew = max2(m, mx);
+      const float msub = (mnew == -INFINITY) ? 0.0f : mnew;
+      const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
+      float ls[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * w], c, -msub));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * w + 1], c, -msub));
+        const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+        ls[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, ls[w & 1], false);
+        pw[w] = __builtin_bit_cast(unsigned, pr);
+      }
+      l = l * alpha + (ls[0] + ls[1]);
+      m = mnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+    }
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const lds_char* pr = base + 16 * c2 * G::kRowBytes + (a_v ^ (64 * db));
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pr);
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pr + 8 * G::kRowBytes));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        const u32x4 w = {pw[4 * c2], pw[4 * c2 + 1], pw[4 * c2 + 2], pw[4 * c2 + 3]};
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, w), acc[db], 0, 0, 0);
+      }
+  };
+  char* st0 = lds_raw;
+  char* st1 = lds_raw + G::kTileBytes;
+  char* st2 = lds_raw + 2 * G::kTileBytes;
+  // The steps run in threes (the registers of a tile rotate with the step) over the tile range
+  // padded to a multiple of three; a padding step fetches zeros and masks every key (its keys are
+  // past hi_split), which leaves m, l and the accumulator exactly as they were. Every step issues
+  // and waits alike, so the compiler sees one regular pattern and adds no waits of its own.
+  issue(t_begin, kreg[0], st0);
+  issue(t_begin + 1, kreg[1], st1);
+  const int t_pad = t_begin + (t_end - t_begin + 2) / 3 * 3;
+  for (int t = t_begin; t < t_pad; t += 3) {
+    step(t, kreg[0], kreg[2], st0, st2);
+    step(t + 1, kreg[1], kreg[0], st1, st0);
+    step(t + 2, kreg[2], kreg[1], st2, st1);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the last padding fetches have landed before the wave ends
+
+  // ---- the partial of this workgroup (same layout as the kernel above) ----
+  const int rows_cap = p.rows_cap;
+  float* ws_acc = p.ws + (size_t)part * rows_cap * D;
+  float* ws_ml = p.ws + (size_t)p.n_partials * rows_cap * D + (size_t)part * rows_cap * 2;
+  const float lt = l + __shfl_xor(l, 32);
+  if (l32 < rows_cap) {
+    float* dst = ws_acc + (size_t)l32 * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 o4 = {acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]};
+        *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * j + 4 * hh) = o4;
+      }
+    if (hh == 0) {
+      ws_ml[2 * l32] = m;
+      ws_ml[2 * l32 + 1] = lt;
+    }
+  }
+}
+
 // One workgroup per output row (b, h, i): combine the row's n_split partials with the merge
 // equations and write O = a / l in BF16 (0 when no key was visible). Thread t owns four columns
-// (d4 = t % (D/4)) of the splits s = j, j + P, ... (j = t / (D/4), P = kMergeThreads / (D/4)), so
-// every thread has several independent loads in flight; the P partial sums are then added by a
-// fixed tree over j, so the result does not depend on timing.
+// (d4 = t % (D/4)) of the splits s = j, j + P, ... (j = t / (D/4), P = kMergeThreads / (D/4)): it
+// loads all of them at once and merges them locally (one round trip to memory), then the P
+// partial triples (m, l, a) are combined by a fixed tree over j with the same equations, so the
+// result does not depend on timing.
 constexpr int kMergeThreads = 1024;
 
 template <int D>
@@ -381,8 +608,7 @@ __global__ __launch_bounds__(kMergeThreads) void pfa_decode_merge_kernel(DParams
   constexpr int C4 = D / 4;              // float4 columns
   constexpr int P = kMergeThreads / C4;  // split lanes
   __shared__ f32x4 red[kMergeThreads];
-  __shared__ float red_m[kMergeThreads];
-  __shared__ float red_l[P];
+  __shared__ float red_m[P], red_l[P];
   const int t = threadIdx.x;
   const int d4 = t % C4, j = t / C4;
   long long id = blockIdx.x;  // (b, h, i)
@@ -395,43 +621,64 @@ __global__ __launch_bounds__(kMergeThreads) void pfa_decode_merge_kernel(DParams
   const int rg = r / kRowsPerGroup, rr = r % kRowsPerGroup;
   const long long part0 = (((long long)b * p.hkv + hk) * p.n_rowgrp + rg) * p.n_split;
   const float* ws_ml = p.ws + (size_t)p.n_partials * p.rows_cap * D;
-  // m* = max over the splits
-  float mloc = -INFINITY;
-  for (int s = t; s < p.n_split; s += kMergeThreads) mloc = max2(mloc, ws_ml[(size_t)(part0 + s) * p.rows_cap * 2 + 2 * rr]);
-  red_m[t] = mloc;
-  __syncthreads();
-  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
-    if (t < w) red_m[t] = max2(red_m[t], red_m[t + w]);
-    __syncthreads();
-  }
-  const float mstar = red_m[0];
-  float lsum = 0.0f;
+  // local merge of this thread's splits (empty splits have m = -inf and l = a = 0)
+  float mloc = -INFINITY, lloc = 0.0f;
   f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (mstar != -INFINITY) {
-#pragma unroll 4
-    for (int s = j; s < p.n_split; s += P) {
-      const size_t q = (size_t)(part0 + s);
-      const float w = __builtin_amdgcn_exp2f(ws_ml[q * p.rows_cap * 2 + 2 * rr] - mstar);  // 0 for empty splits
-      lsum = __builtin_fmaf(w, ws_ml[q * p.rows_cap * 2 + 2 * rr + 1], lsum);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p.ws + (q * p.rows_cap + rr) * D + 4 * d4);
-      a += w * v;
+  for (int s0 = j; s0 < p.n_split; s0 += 4 * P) {
+    float ms[4], ls[4];
+    f32x4 vs[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // four splits' loads in flight before any use
+      const int sp = s0 + u * P;
+      if (sp < p.n_split) {
+        const size_t q = (size_t)(part0 + sp);
+        ms[u] = ws_ml[q * p.rows_cap * 2 + 2 * rr];
+        ls[u] = ws_ml[q * p.rows_cap * 2 + 2 * rr + 1];
+        vs[u] = *reinterpret_cast<const f32x4*>(p.ws + (q * p.rows_cap + rr) * D + 4 * d4);
+      } else {
+        ms[u] = -INFINITY;
+        ls[u] = 0.0f;
+        vs[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float mn = max2(mloc, ms[u]);
+      if (mn != -INFINITY) {
+        const float w0 = __builtin_amdgcn_exp2f(mloc - mn), w1 = __builtin_amdgcn_exp2f(ms[u] - mn);
+        lloc = lloc * w0 + ls[u] * w1;
+        a = a * w0 + vs[u] * w1;
+        mloc = mn;
+      }
     }
   }
   red[t] = a;
-  if (d4 == 0) red_l[j] = lsum;
+  if (d4 == 0) {
+    red_m[j] = mloc;
+    red_l[j] = lloc;
+  }
   __syncthreads();
   // fixed tree over the split lanes j (red[j * C4 + d4])
   for (int w = P / 2; w > 0; w >>= 1) {
+    float m1 = 0.0f, m2 = 0.0f, mn = 0.0f;
     if (j < w) {
-      red[t] += red[t + w * C4];
-      if (d4 == 0) red_l[j] += red_l[j + w];
+      m1 = red_m[j];
+      m2 = red_m[j + w];
+      mn = max2(m1, m2);
+      if (mn != -INFINITY) {
+        const float w0 = __builtin_amdgcn_exp2f(m1 - mn), w1 = __builtin_amdgcn_exp2f(m2 - mn);
+        red[t] = red[t] * w0 + red[t + w * C4] * w1;
+        if (d4 == 0) red_l[j] = red_l[j] * w0 + red_l[j + w] * w1;
+      }
     }
+    __syncthreads();
+    if (j < w && d4 == 0) red_m[j] = mn;
     __syncthreads();
   }
   if (j == 0) {
     float lt = red_l[0];
     // an attention sink adds e^sink to the normaliser, relative to the merged maximum
-    if (p.sinks != nullptr && lt > 0.0f) lt += __builtin_amdgcn_exp2f(__builtin_fmaf(p.sinks[h], kLog2e, -mstar));
+    if (p.sinks != nullptr && lt > 0.0f) lt += __builtin_amdgcn_exp2f(__builtin_fmaf(p.sinks[h], kLog2e, -red_m[0]));
     const f32x4 at = red[d4];
     uint16_t* orow = o + (((long long)b * p.hq + h) * p.lq + i) * D + 4 * d4;
 #pragma unroll
@@ -472,7 +719,10 @@ int launch_decode_variant(const pfa::Launch& L, const pfa::DecodePlan& plan, voi
   hipStream_t stream = static_cast<hipStream_t>(L.stream);
   void* args[] = {&p};
   const void* fn =
-      L.key_mask ? (sc ? reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, true, true>)
+      (RB == 1 && !L.key_mask)
+          ? (sc ? reinterpret_cast<const void*>(&pfa_decode_kreg_kernel<D, true>)
+                : reinterpret_cast<const void*>(&pfa_decode_kreg_kernel<D, false>))
+      : L.key_mask ? (sc ? reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, true, true>)
                        : reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, true, false>))
                  : (sc ? reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, false, true>)
                        : reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, false, false>));
