@@ -201,9 +201,14 @@ def kernel_name(workload_name: str) -> str:
         return "pfa_prefill_kernel<%d, 0>" % VARLEN_CONFIGS[workload_name]["D"]
     c = CONFIGS[workload_name]
     if c.get("entry") == "decode":
-        return "pfa_decode_split_kernel<%d, %d, %s, %s> + pfa_decode_merge_kernel<%d>" % (
-            c["D"], 2 if (c["Hq"] // c["Hkv"]) * c["L"] > 32 else 1, "true" if c["key_padding"] else "false",
-            "true" if c.get("softcap") else "false", c["D"])
+        rows = (c["Hq"] // c["Hkv"]) * c["L"]
+        sc = "true" if c.get("softcap") else "false"
+        if rows <= 32 and not c["key_padding"]:
+            split = "pfa_decode_kreg_kernel<%d, %s>" % (c["D"], sc)
+        else:
+            split = "pfa_decode_split_kernel<%d, %d, %s, %s>" % (
+                c["D"], 2 if rows > 32 else 1, "true" if c["key_padding"] else "false", sc)
+        return "%s + pfa_decode_merge_kernel<%d>" % (split, c["D"])
     mode = (1 if c["key_padding"] else 0) | (2 if c.get("entry") == "ring" else 0) | \
         (4 if c.get("softcap") else 0) | (8 if c.get("bias") else 0) | (16 if c.get("block_sel") else 0)
     suffix = " (after pfa_ring_append_kernel)" if c.get("entry") == "ring" else ""
