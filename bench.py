@@ -152,43 +152,36 @@ def blas_single_thread():
 
 
 def cpu_baseline(workers: int, budget_s: float = 20.0) -> dict:
-    """The oracle as it stands, on a bounded sample of the 8K chunk: heads taken one by one (all
-    2048 rows each) until about `budget_s` of wall time has passed."""
-    import numpy as np
-
+    """The oracle as it stands, on a bounded sample of the bench step: the query heads of the 8K
+    chunk, then of the 32K chunk, one KV group at a time (all rows of each head), until about
+    `budget_s` of wall time has passed or the whole step is done."""
     from oracle import oracle_sdpa
     from workloads import CONFIGS, make_inputs
 
-    c = CONFIGS["mid_ctx_8k"]
-    x = make_inputs("mid_ctx_8k", seed=0)
-    G = c["Hq"] // c["Hkv"]
-    per_head_pairs = visible_pairs(dict(c, B=1, Hq=1))
-    heads = 0
+    done = []
+    total_flops = 0.0
     limit = blas_single_thread()
     limit.__enter__()
     t0 = time.perf_counter()
-    step = max(1, workers // 8)
-    while time.perf_counter() - t0 < budget_s and heads < c["Hq"]:
-        h1 = min(c["Hq"], heads + step)
-        hk0, hk1 = heads // G, (h1 - 1) // G + 1
-        # the oracle maps query head h to KV head h // G; slice whole groups and keep the map
-        q = x["q"][:, heads:h1]
-        k = x["k"][:, hk0:hk1]
-        v = x["v"][:, hk0:hk1]
-        if (heads % G) != 0 or (h1 - heads) % G != 0:
-            # partial group: run head by head against its own KV head
-            for h in range(heads, h1):
-                oracle_sdpa(x["q"][:, h:h + 1], x["k"][:, h // G:h // G + 1], x["v"][:, h // G:h // G + 1],
-                            x["scale"], c["causal_offset"], c["window"], None, workers=workers)
-        else:
-            oracle_sdpa(q, k, v, x["scale"], c["causal_offset"], c["window"], None, workers=workers)
-        heads = h1
+    for name in ("mid_ctx_8k", "long_ctx_32k"):
+        c = CONFIGS[name]
+        x = make_inputs(name, seed=0)
+        G = c["Hq"] // c["Hkv"]
+        per_head = 4.0 * c["D"] * visible_pairs(dict(c, B=1, Hq=1))
+        heads = 0
+        for hk in range(c["Hkv"]):
+            if time.perf_counter() - t0 >= budget_s:
+                break
+            # one KV group: its G query heads against KV head hk (the oracle maps h -> h // G)
+            oracle_sdpa(x["q"][:, hk * G:(hk + 1) * G], x["k"][:, hk:hk + 1], x["v"][:, hk:hk + 1], x["scale"],
+                        c["causal_offset"], c["window"], None, workers=workers)
+            heads += G
+            total_flops += G * per_head
+        done.append(f"{name} {heads}/{c['Hq']} heads")
     dt = time.perf_counter() - t0
     limit.__exit__(None, None, None)
-    flops = 4.0 * c["D"] * per_head_pairs * heads
-    del np
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
-            "sample": f"mid_ctx_8k (L=2048, S=8192, D=128): {heads} of {c['Hq']} query heads, all rows, "
+    return {"value": total_flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"the bench step's chunks (all rows of each head, whole KV groups): {', '.join(done)}; "
                       f"fp64 NumPy, {dt:.1f} s wall, {workers} threads x 1 BLAS thread"}
 
 
