@@ -984,21 +984,26 @@ int launch_variant(const pfa::Launch& L) {
 }
 
 // Rotating-cache append: row i of K_new / V_new [B, Hkv, L, D] (position pos0 + i) goes to slot
-// (pos0 + i) mod ring of K_ring / V_ring [B, Hkv, ring, D]. One thread per 16 bytes.
+// (pos0 + i) mod ring of K_ring / V_ring [B, Hkv, ring, D]. One thread per 16 bytes; blockIdx.y
+// (striding by gridDim.y) is the (b, kv head) pair, x the 16-byte chunk within its L rows. The
+// slot is p0 + i with p0 = pos0 mod ring, wrapped once (the ring holds at least L slots).
 __global__ __launch_bounds__(256) void pfa_ring_append_kernel(const uint4* __restrict__ kn, const uint4* __restrict__ vn,
                                                               uint4* __restrict__ kr, uint4* __restrict__ vr,
-                                                              long long n_chunks, int L, int ring, int pos0,
-                                                              int chunks_per_row) {
-  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n_chunks) return;
-  const int c = (int)(t % chunks_per_row);
-  long long r = t / chunks_per_row;  // (b * Hkv + hk) * L + i
-  const int i = (int)(r % L);
-  const long long bh = r / L;
-  const long long slot = ((long long)pos0 + i) % ring;
-  const long long dst = (bh * ring + slot) * chunks_per_row + c;
-  kr[dst] = kn[t];
-  vr[dst] = vn[t];
+                                                              long long n_bh, int L, int ring, int p0,
+                                                              int cpr_log2) {
+  const long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // chunk within one (b, hk)
+  const long long per_bh = (long long)L << cpr_log2;
+  if (j >= per_bh) return;
+  const int i = (int)(j >> cpr_log2);
+  const long long c = j & ((1 << cpr_log2) - 1);
+  int slot = p0 + i;
+  if (slot >= ring) slot -= ring;
+  for (long long bh = blockIdx.y; bh < n_bh; bh += gridDim.y) {
+    const long long src = bh * per_bh + j;
+    const long long dst = ((bh * ring + slot) << cpr_log2) + c;
+    kr[dst] = kn[src];
+    vr[dst] = vn[src];
+  }
 }
 
 }  // namespace
@@ -1007,12 +1012,14 @@ namespace pfa {
 
 int launch_ring_append(const void* k_new, const void* v_new, void* k_ring, void* v_ring, int B, int Hkv, int L,
                        int D, int ring, int pos0, void* stream) {
-  const int cpr = D / 8;
-  const long long n = (long long)B * Hkv * L * cpr;
-  const long long blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(pfa_ring_append_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+  const int cpr_log2 = D == 128 ? 4 : 3;  // 16-byte chunks per row: D / 8
+  const long long per_bh = (long long)L << cpr_log2;
+  const long long n_bh = (long long)B * Hkv;
+  const long long bx = (per_bh + 255) / 256;
+  const unsigned by = (unsigned)(n_bh < 65535 ? n_bh : 65535);
+  hipLaunchKernelGGL(pfa_ring_append_kernel, dim3((unsigned)bx, by), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new), static_cast<uint4*>(k_ring),
-                     static_cast<uint4*>(v_ring), n, L, ring, pos0, cpr);
+                     static_cast<uint4*>(v_ring), n_bh, L, ring, pos0 % ring, cpr_log2);
   return hipGetLastError() == hipSuccess ? PFA_OK : PFA_ERR_LAUNCH;
 }
 
