@@ -28,7 +28,9 @@
 //    of three stages: tile t+1 lands while tile t's K and tile t-1's V are read. Rows are
 //    unpadded; 16-byte chunks are XOR-swizzled per row so both the K reads (ds_read_b128, one row
 //    per lane) and the V transpose reads (four rows per 16 lanes) are free of bank conflicts.
-//  * Scores are scaled by scale*log2(e) inside the exp2 argument (one FMA per score).
+//  * Scores are scaled by scale*log2(e) inside the exp2 argument (one FMA per score), in FP32:
+//    folding the scale into Q instead rounds q*scale*log2(e) to BF16, an error proportional to the
+//    logit, which breaks the accuracy bound once logits reach tens of units.
 //  * The tile range of a workgroup is bounded by the causal and window edges; with a key mask a
 //    per-tile "any valid" bitmap (64 tiles per ballot) lets the loop jump over empty tiles; waves
 //    whose own rows see nothing of a tile skip its arithmetic. Elementwise masks run only on
