@@ -797,23 +797,30 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   // a wave runs its MFMA phase in one half and its softmax phase in the other (group A: MFMA
   // first). Group A issues the fetch of `nxt` right after its MFMA phase; it lands during the
   // second half and is waited for before the closing barrier.
-  {
-    // zero every stage once, so that a stage never read by a real tile holds finite data
-    uint4* z = reinterpret_cast<uint4*>(lds_raw);
-    for (int i = tid; i < kStages * G::kStageBytes / 16; i += kThreads) z[i] = make_uint4(0, 0, 0, 0);
-  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int t = 0; t < 8; ++t) pb[i][t] = (__bf16)0.0f;
-  __syncthreads();
   int packed = next_tile(kt_lo);
   int cur = packed >> 1;
   bool all_cur = packed & 1;
-  if (cur < kt_hi) {
-    issue(cur, 0);
-    finish(0);
+  // The first tile goes to stage 0 (every byte of it written by the fetch); the other stages are
+  // zeroed once, so that a stage read before any tile lands there holds finite data. The zeroing
+  // is done by fetches from an empty buffer descriptor (they write zeros), issued behind the first
+  // tile's fetch so that both are in flight together.
+  if (cur < kt_hi) issue(cur, 0);
+  {
+    constexpr int kPerWave = G::kStageBytes / 1024 / kWaves;  // 1 KB fetches per wave and stage
+    unsigned zoff[kPerWave];
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) zoff[j] = 0u;
+#pragma unroll
+    for (int st = 1; st < kStages; ++st)
+      dma_rows<kPerWave>(reinterpret_cast<const void*>(p.q), 0,
+                         (lds_char*)lds_raw + st * G::kStageBytes + wave * kPerWave * 1024, zoff);
   }
+  if (cur < kt_hi) finish(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the zero fills have landed too
   __syncthreads();
   int prv = kt_hi;
   TileView tv_cur{}, tv_prv{};
