@@ -58,6 +58,10 @@ CASES = [
     ("l8_more_rows_than_keys", 1, 4, 4, 128, 8, 5, 0, 0, None),
     ("l1_s1", 2, 2, 1, 64, 1, 1, 0, 0, None),
     ("l64_window_d64", 1, 8, 8, 64, 64, 2000, 1936, 100, None),
+    # exactly 32 rows per KV head (the register-K kernel's limit), a window and a ragged last tile
+    ("l8_g4_rows32_window", 2, 16, 4, 128, 8, 1000, 992, 300, None),
+    # one tile per split and keys shorter than a tile for some rows (padding steps of the split kernel)
+    ("l2_g2_s70", 3, 4, 2, 128, 2, 70, 68, 0, None),
 ]
 
 
