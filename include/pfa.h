@@ -137,7 +137,7 @@ int prefill_attn_gqa_ex(const void* Q, const void* K, const void* V,
  *            O[i] = sum_j e^(s_ij) V_j / (sum_j e^(s_ij) + e^sinks[h]) over the visible keys j,
  *            s_ij the final (scaled, soft-capped, biased) score. The sink is used as given (not
  *            scaled). Values finite or -inf (-inf = no sink for that head). A row without a
- *            visible key still gives zeros. Prefill and decode entry points.
+ *            visible key still gives zeros. Prefill (dense and packed) and decode entry points.
  *   block_sel  NULL, or a DEVICE uint8 block bitmap (TensorFold PR "What changes": MiniMax-M3's
  *            prompt attention adds a block bitmap, SEL; the pages give no layout, and the reading
  *            taken is: with query blocks of block_q rows and key blocks of block_k keys, key j is
@@ -205,6 +205,15 @@ int prefill_attn_gqa_varlen(const void* Q, const void* K, const void* V,
                             int n_seq, int max_seqlen_q, int total_q, int total_k,
                             int Hq, int Hkv, int D, float scale, int causal, int window,
                             void* O, void* stream);
+
+/* prefill_attn_gqa_varlen with options (see pfa_options): flags, softcap and sinks apply as in
+ * prefill_attn_gqa_opt (sinks indexed by query head); bias and block_sel are per dense row and are
+ * rejected here (PFA_ERR_MASK_ARGS). */
+int prefill_attn_gqa_varlen_opt(const void* Q, const void* K, const void* V,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int n_seq, int max_seqlen_q, int total_q, int total_k,
+                                int Hq, int Hkv, int D, float scale, int causal, int window,
+                                void* O, void* stream, const pfa_options* opts);
 
 /*
  * prefill_attn_gqa_ring -- causal (optionally sliding-window) prefill of a chunk against a rotating

@@ -15,12 +15,13 @@ taken for unequal lengths: the rows are the last Lq positions of the sequence's 
 after its cached prefix, the alignment of tiny-llm Week 2 Day 5 Task 2 and of the tinygrad prefill
 mask), so j <= i + (Lk - Lq); this reduces to the page's rule when Lq == Lk. Window term (as in
 ``oracle.sdpa``): j >= i + (Lk - Lq) - W + 1 when W > 0. A row with no visible key outputs zeros.
+The logit soft-cap and the attention sinks are those of ``oracle.sdpa`` (same functions).
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .sdpa import _softmax_rows_times_v, _widen, kv_head_of
+from .sdpa import _softmax_rows_times_v, _widen, kv_head_of, soft_cap
 
 
 def varlen_visible(Lq: int, Lk: int, causal: bool, window: int) -> np.ndarray:
@@ -36,9 +37,11 @@ def varlen_visible(Lq: int, Lk: int, causal: bool, window: int) -> np.ndarray:
     return vis
 
 
-def oracle_varlen(q, k, v, cu_q, cu_k, scale, causal: bool = True, window: int = 0) -> np.ndarray:
+def oracle_varlen(q, k, v, cu_q, cu_k, scale, causal: bool = True, window: int = 0, softcap: float = 0.0,
+                  sinks=None) -> np.ndarray:
     """Packed variable-length SDPA in fp64. q: [total_q, Hq, D], k/v: [total_k, Hkv, D] as bf16 bits
-    (uint16) or floats; cu_q / cu_k: prefix sums of n_seq + 1 entries. Returns fp64 [total_q, Hq, D]."""
+    (uint16) or floats; cu_q / cu_k: prefix sums of n_seq + 1 entries; softcap > 0: logit soft-cap;
+    sinks: [Hq] sink logits or None. Returns fp64 [total_q, Hq, D]."""
     q, k, v = _widen(q), _widen(k), _widen(v)
     total_q, Hq, D = q.shape
     Hkv = k.shape[1]
@@ -60,12 +63,14 @@ def oracle_varlen(q, k, v, cu_q, cu_k, scale, causal: bool = True, window: int =
             hk = kv_head_of(h, Hq, Hkv)
             if Lk == 0:
                 continue  # no keys: zeros
-            scores = scale * (q[q0:q1, h] @ k[k0:k1, hk].T) + add
-            out[q0:q1, h] = _softmax_rows_times_v(scores, v[k0:k1, hk])
+            scores = soft_cap(scale * (q[q0:q1, h] @ k[k0:k1, hk].T), float(softcap)) + add
+            out[q0:q1, h] = _softmax_rows_times_v(scores, v[k0:k1, hk],
+                                                  None if sinks is None else float(np.float64(sinks[h])))
     return out
 
 
-def oracle_varlen_rows(q, k, v, cu_q, cu_k, scale, causal, window, picks) -> np.ndarray:
+def oracle_varlen_rows(q, k, v, cu_q, cu_k, scale, causal, window, picks, softcap: float = 0.0,
+                       sinks=None) -> np.ndarray:
     """Oracle output for selected (packed row, query head) pairs only: fp64 [len(picks), D]. Used at
     full workload sizes, where every row would take too long."""
     Hq, Hkv = q.shape[1], k.shape[1]
@@ -83,6 +88,7 @@ def oracle_varlen_rows(q, k, v, cu_q, cu_k, scale, causal, window, picks) -> np.
             res.append(np.zeros(v.shape[-1]))
             continue
         kk, vv = _widen(k[k0:k1, hk]), _widen(v[k0:k1, hk])
-        scores = float(np.float64(scale)) * (_widen(q[r:r + 1, h]) @ kk.T) + np.where(vis, 0.0, -np.inf)
-        res.append(_softmax_rows_times_v(scores, vv)[0])
+        scores = soft_cap(float(np.float64(scale)) * (_widen(q[r:r + 1, h]) @ kk.T), float(softcap))
+        scores = scores + np.where(vis, 0.0, -np.inf)
+        res.append(_softmax_rows_times_v(scores, vv, None if sinks is None else float(np.float64(sinks[h])))[0])
     return np.array(res)

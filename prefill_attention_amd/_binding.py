@@ -24,6 +24,7 @@ STATUS = {
 }
 DECODE_MAX_L = 64
 EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_opt", "prefill_attn_gqa_varlen",
+           "prefill_attn_gqa_varlen_opt",
            "prefill_attn_gqa_ring", "prefill_attn_gqa_decode", "prefill_attn_gqa_decode_opt",
            "pfa_decode_workspace_bytes", "pfa_status_str", "pfa_version")
 
@@ -65,6 +66,8 @@ def library() -> ctypes.CDLL:
         lib.prefill_attn_gqa_varlen.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, ci,
                                                 vp, vp]
         lib.prefill_attn_gqa_varlen.restype = ci
+        lib.prefill_attn_gqa_varlen_opt.argtypes = lib.prefill_attn_gqa_varlen.argtypes + [ctypes.POINTER(Options)]
+        lib.prefill_attn_gqa_varlen_opt.restype = ci
         lib.prefill_attn_gqa_decode.argtypes = sig[:-1] + [vp, ctypes.c_int64, vp]
         lib.prefill_attn_gqa_decode.restype = ci
         lib.prefill_attn_gqa_decode_opt.argtypes = sig[:-1] + [vp, ctypes.c_int64, vp, ctypes.POINTER(Options)]
@@ -236,22 +239,29 @@ def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True
 def prefill_attn_gqa_varlen_raw(q_ptr: int, k_ptr: int, v_ptr: int, cu_q_ptr: int, cu_k_ptr: int,
                                 n_seq: int, max_seqlen_q: int, total_q: int, total_k: int, Hq: int,
                                 Hkv: int, D: int, scale: float, causal: bool, window: int,
-                                o_ptr: int, stream: int | None) -> int:
+                                o_ptr: int, stream: int | None, flags: int = 0, softcap: float = 0.0,
+                                sinks_ptr: int | None = None) -> int:
     """Direct C-ABI call of the packed variable-length entry point; returns the status code."""
-    return int(library().prefill_attn_gqa_varlen(
+    if flags == 0 and softcap == 0.0 and not sinks_ptr:
+        return int(library().prefill_attn_gqa_varlen(
+            q_ptr, k_ptr, v_ptr, cu_q_ptr, cu_k_ptr, n_seq, max_seqlen_q, total_q, total_k, Hq, Hkv, D,
+            ctypes.c_float(scale), 1 if causal else 0, window, o_ptr, stream or None))
+    opts = Options(flags, softcap, None, 0, 0, 0, sinks_ptr or None)
+    return int(library().prefill_attn_gqa_varlen_opt(
         q_ptr, k_ptr, v_ptr, cu_q_ptr, cu_k_ptr, n_seq, max_seqlen_q, total_q, total_k, Hq, Hkv, D,
-        ctypes.c_float(scale), 1 if causal else 0, window, o_ptr, stream or None))
+        ctypes.c_float(scale), 1 if causal else 0, window, o_ptr, stream or None, ctypes.byref(opts)))
 
 
 def prefill_attn_gqa_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *,
                             scale: float | None = None, causal: bool = True, window: int = 0,
-                            out=None, stream=None):
+                            out=None, no_skip: bool = False, softcap: float = 0.0, sinks=None, stream=None):
     """Packed variable-length grouped-query attention on torch tensors.
 
     q: bf16 [total_q, Hq, D]; k, v: bf16 [total_k, Hkv, D]; cu_seqlens_q / cu_seqlens_k: int32
     [n_seq + 1] prefix sums on the same device. max_seqlen_q bounds every sequence's query
     length. With causal=True local row i of a sequence sees local keys j <= i + (Lk - Lq).
-    Returns `out` (allocated if None), bf16 [total_q, Hq, D].
+    no_skip, softcap and sinks as in prefill_attn_gqa. Returns `out` (allocated if None), bf16
+    [total_q, Hq, D].
     """
     import torch
 
@@ -289,7 +299,8 @@ def prefill_attn_gqa_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: i
         rc = prefill_attn_gqa_varlen_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
                                          cu_seqlens_k.data_ptr(), n_seq, int(max_seqlen_q), total_q, total_k,
                                          Hq, Hkv, D, float(scale), bool(causal), int(window), out.data_ptr(),
-                                         stream_ptr)
+                                         stream_ptr, FLAG_NO_SKIP if no_skip else 0, float(softcap),
+                                         _sinks_ptr(sinks, Hq, q.device))
     if rc != 0:
         raise PfaError(rc, status_str(rc))
     return out

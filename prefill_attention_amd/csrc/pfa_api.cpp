@@ -180,10 +180,11 @@ int prefill_attn_gqa(const void* Q, const void* K, const void* V, int B, int Hq,
                              key_mask, O, stream, 0u);
 }
 
-int prefill_attn_gqa_varlen(const void* Q, const void* K, const void* V,
-                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seq,
-                            int max_seqlen_q, int total_q, int total_k, int Hq, int Hkv, int D,
-                            float scale, int causal, int window, void* O, void* stream) {
+int prefill_attn_gqa_varlen_opt(const void* Q, const void* K, const void* V,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seq,
+                                int max_seqlen_q, int total_q, int total_k, int Hq, int Hkv, int D,
+                                float scale, int causal, int window, void* O, void* stream,
+                                const pfa_options* opts) {
   if (!Q || !K || !V || !O || !cu_seqlens_q || !cu_seqlens_k) return PFA_ERR_NULL;
   if (n_seq < 1 || max_seqlen_q < 1 || total_q < 1 || total_k < 1 || Hq < 1 || Hkv < 1 || D < 1)
     return PFA_ERR_SIZE;
@@ -212,6 +213,14 @@ int prefill_attn_gqa_varlen(const void* Q, const void* K, const void* V,
       overlaps(o, range(V, kv_elems * 2)) || overlaps(o, range(cu_seqlens_q, cu_bytes)) ||
       overlaps(o, range(cu_seqlens_k, cu_bytes)))
     return PFA_ERR_ALIAS;
+  const unsigned flags = opts ? opts->flags : 0u;
+  const float softcap = opts ? opts->softcap : 0.0f;
+  if (flags & ~PFA_FLAG_NO_SKIP) return PFA_ERR_FLAGS;
+  if (!std::isfinite(softcap) || softcap < 0.0f) return PFA_ERR_SCALE;
+  // the packed layout takes no additive bias and no block bitmap (both are laid out per dense row)
+  if (opts && (opts->bias || opts->block_sel)) return PFA_ERR_MASK_ARGS;
+  const int rc = check_sinks(opts, Hq, o);
+  if (rc != PFA_OK) return rc;
   pfa::Launch p;
   p.q = Q;
   p.k = K;
@@ -229,14 +238,24 @@ int prefill_attn_gqa_varlen(const void* Q, const void* K, const void* V,
   p.causal = causal ? 1 : 0;
   p.causal_offset = 0;  // per sequence: Lk - Lq
   p.window = (causal && window > 0) ? window : 0;
-  p.flags = 0;
+  p.flags = flags;
   p.stream = stream;
+  p.softcap = softcap;
+  p.sinks = opts ? opts->sinks : nullptr;
   p.cu_q = cu_seqlens_q;
   p.cu_k = cu_seqlens_k;
   p.total_q = total_q;
   p.total_k = total_k;
   if (pfa::grid_blocks(p) > INT_MAX) return PFA_ERR_SIZE;
   return pfa::launch_prefill(p);
+}
+
+int prefill_attn_gqa_varlen(const void* Q, const void* K, const void* V,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seq,
+                            int max_seqlen_q, int total_q, int total_k, int Hq, int Hkv, int D,
+                            float scale, int causal, int window, void* O, void* stream) {
+  return prefill_attn_gqa_varlen_opt(Q, K, V, cu_seqlens_q, cu_seqlens_k, n_seq, max_seqlen_q, total_q, total_k,
+                                     Hq, Hkv, D, scale, causal, window, O, stream, nullptr);
 }
 
 }  // extern "C"

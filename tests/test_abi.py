@@ -379,3 +379,20 @@ def test_block_bitmap_not_on_decode(lib):
     assert pfa.prefill_attn_gqa_decode_raw(d["q"], d["k"], d["v"], d["B"], d["Hq"], d["Hkv"], d["L"], d["S"],
                                            d["D"], d["scale"], d["off"], d["window"], None, d["o"], d["ws"],
                                            need, None, 0.0, 0, O + 2) == 7
+
+
+def vocall(flags=0, softcap=0.0, sinks=None, bias=None, sel=None):
+    a = dict(VGOOD)
+    opts = pfa.Options(flags, softcap, bias, 0, 0, 0, sinks, sel, 32 if sel else 0, 64 if sel else 0, 0, 0, 1)
+    return pfa.library().prefill_attn_gqa_varlen_opt(
+        a["q"], a["k"], a["v"], a["cq"], a["ck"], a["n"], a["maxq"], a["tq"], a["tk"], a["Hq"], a["Hkv"], a["D"],
+        ctypes.c_float(a["scale"]), 1 if a["causal"] else 0, a["window"], a["o"], None, ctypes.byref(opts))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=2), 9), (dict(softcap=-1.0), 6), (dict(softcap=float("inf")), 6),
+    (dict(bias=BIAS), 5), (dict(sel=SEL), 5),            # per dense row: not on the packed layout
+    (dict(sinks=SINKS + 2), 7), (dict(sinks=O + 4), 8),
+], ids=lambda x: str(x))
+def test_varlen_options_rejected(lib, kw, code):
+    assert vocall(**kw) == code

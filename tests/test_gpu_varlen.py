@@ -126,3 +126,40 @@ def test_varlen_full_size_sampled_rows():
     ref = oracle_varlen_rows(x["q"], x["k"], x["v"], x["cu_q"], x["cu_k"], x["scale"], True, 0, picks)
     mine = np.array([got[r, h] for r, h in picks])
     check_close(mine, ref, "varlen_causal_b8 sampled rows")
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 100)])
+def test_varlen_options_parity_and_skip_identity(D, causal, window):
+    """Soft-cap and attention sinks on the packed layout against the oracle; skip == no-skip bit for
+    bit; each sequence bit-identical to the dense entry point with the same options."""
+    lq, lk = LENGTHS["ragged"]
+    x = make_varlen_inputs("varlen_chunks_b5", seed=23, lengths_q=lq, lengths_k=lk, D=D)
+    Hq = x["Hq"]
+    sinks = (np.random.default_rng(24).standard_normal(Hq) * 2.0).astype(np.float32)
+    sinks[0] = -np.inf
+    print(f"varlen options D={D} causal={causal} window={window}", flush=True)
+    q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    cq, ck = dev_i32(x["cu_q"]), dev_i32(x["cu_k"])
+    st = torch.from_numpy(sinks).to(DEV)
+    kw = dict(scale=float(x["scale"]), causal=causal, window=window, softcap=4.0, sinks=st)
+    got = pfa.prefill_attn_gqa_varlen(q, k, v, cq, ck, x["max_seqlen_q"], **kw)
+    got_ns = pfa.prefill_attn_gqa_varlen(q, k, v, cq, ck, x["max_seqlen_q"], no_skip=True, **kw)
+    torch.cuda.synchronize()
+    ref = oracle_varlen(x["q"], x["k"], x["v"], x["cu_q"], x["cu_k"], x["scale"], causal, window, softcap=4.0,
+                        sinks=sinks.astype(np.float64))
+    check_close(got.double().cpu().numpy(), ref, f"options D={D} causal={causal} W={window}")
+    assert torch.equal(got.view(torch.int16), got_ns.view(torch.int16))
+    c_q, c_k = x["cu_q"], x["cu_k"]
+    for b in range(len(lq)):
+        if lq[b] == 0 or lk[b] == 0 or (causal and lk[b] < lq[b]):
+            continue
+        qd = q[c_q[b]:c_q[b + 1]].permute(1, 0, 2).contiguous()[None]
+        kd = k[c_k[b]:c_k[b + 1]].permute(1, 0, 2).contiguous()[None]
+        vd = v[c_k[b]:c_k[b + 1]].permute(1, 0, 2).contiguous()[None]
+        dense = pfa.prefill_attn_gqa(qd, kd, vd, scale=float(x["scale"]), causal=causal,
+                                     causal_offset=(lk[b] - lq[b]) if causal else None, window=window,
+                                     softcap=4.0, sinks=st)
+        torch.cuda.synchronize()
+        mine = got[c_q[b]:c_q[b + 1]].permute(1, 0, 2)[None]
+        assert torch.equal(mine.view(torch.int16), dense.view(torch.int16)), f"sequence {b}"

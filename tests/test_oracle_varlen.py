@@ -83,8 +83,30 @@ def pin_sequences_independent():
     assert np.all(base[cq[2]:cq[3]] == 0.0)
 
 
+def pin_options_match_dense():
+    """With a soft-cap and sink logits, each packed sequence is the dense oracle on that sequence
+    with the same options (pinned in test_oracle.py), and scalar brute force on tiny sequences."""
+    lq, lk = [20, 33, 4], [50, 33, 9]  # Lk >= Lq: the dense offset Lk - Lq is a causal one
+    x = make_varlen_inputs("varlen_chunks_b5", seed=17, lengths_q=lq, lengths_k=lk, D=16, Hq=4, Hkv=2)
+    sinks = np.array([0.3, -1.0, 2.0, -np.inf])
+    got = oracle_varlen(x["q"], x["k"], x["v"], x["cu_q"], x["cu_k"], x["scale"], True, 0, softcap=2.5, sinks=sinks)
+    cq, ck = x["cu_q"], x["cu_k"]
+    for b in range(3):
+        ref = oracle_sdpa(to_dense(x["q"], cq[b], cq[b + 1]), to_dense(x["k"], ck[b], ck[b + 1]),
+                          to_dense(x["v"], ck[b], ck[b + 1]), x["scale"], causal_offset=lk[b] - lq[b],
+                          softcap=2.5, sinks=sinks)
+        assert np.allclose(np.transpose(got[cq[b]:cq[b + 1]], (1, 0, 2)), ref[0], atol=1e-12, rtol=0)
+    y = make_varlen_inputs("varlen_chunks_b5", seed=19, lengths_q=[3, 2], lengths_k=[4, 2], D=4, Hq=2, Hkv=1)
+    got = oracle_varlen(y["q"], y["k"], y["v"], y["cu_q"], y["cu_k"], y["scale"], True, 0, softcap=1.5,
+                        sinks=sinks[:2])
+    for b, (a0, a1, k0, k1) in enumerate([(0, 3, 0, 4), (3, 5, 4, 6)]):
+        ref = brute_sdpa(to_dense(y["q"], a0, a1), to_dense(y["k"], k0, k1), to_dense(y["v"], k0, k1), y["scale"],
+                         causal_offset=(k1 - k0) - (a1 - a0), softcap=1.5, sinks=sinks[:2])
+        assert np.allclose(np.transpose(got[a0:a1], (1, 0, 2)), ref[0], atol=1e-12, rtol=0)
+
+
 PINS = [pin_single_sequence_is_dense, pin_equal_length_pair_count, pin_more_rows_than_keys,
-        pin_brute_force_ragged, pin_sequences_independent]
+        pin_brute_force_ragged, pin_sequences_independent, pin_options_match_dense]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
