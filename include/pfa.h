@@ -137,7 +137,7 @@ int prefill_attn_gqa_ex(const void* Q, const void* K, const void* V,
  *            O[i] = sum_j e^(s_ij) V_j / (sum_j e^(s_ij) + e^sinks[h]) over the visible keys j,
  *            s_ij the final (scaled, soft-capped, biased) score. The sink is used as given (not
  *            scaled). Values finite or -inf (-inf = no sink for that head). A row without a
- *            visible key still gives zeros. Prefill (dense and packed) and decode entry points.
+ *            visible key still gives zeros. Prefill (dense, packed, ring) and decode entry points.
  *   block_sel  NULL, or a DEVICE uint8 block bitmap (TensorFold PR "What changes": MiniMax-M3's
  *            prompt attention adds a block bitmap, SEL; the pages give no layout, and the reading
  *            taken is: with query blocks of block_q rows and key blocks of block_k keys, key j is
@@ -246,6 +246,15 @@ int prefill_attn_gqa_ring(const void* Q, const void* K_new, const void* V_new,
                           void* K_ring, void* V_ring,
                           int B, int Hq, int Hkv, int L, int pos0, int ring, int D,
                           float scale, int window, void* O, void* stream);
+
+/* prefill_attn_gqa_ring with options (see pfa_options): flags, softcap and sinks apply as in
+ * prefill_attn_gqa_opt; bias and block_sel are rejected (PFA_ERR_MASK_ARGS); the sink logits must
+ * not overlap O or the rings (PFA_ERR_ALIAS). On any error nothing is enqueued. */
+int prefill_attn_gqa_ring_opt(const void* Q, const void* K_new, const void* V_new,
+                              void* K_ring, void* V_ring,
+                              int B, int Hq, int Hkv, int L, int pos0, int ring, int D,
+                              float scale, int window, void* O, void* stream,
+                              const pfa_options* opts);
 
 /*
  * prefill_attn_gqa_decode -- the operation of prefill_attn_gqa for a short query chunk (one-token

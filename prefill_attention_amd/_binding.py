@@ -24,7 +24,7 @@ STATUS = {
 }
 DECODE_MAX_L = 64
 EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_opt", "prefill_attn_gqa_varlen",
-           "prefill_attn_gqa_varlen_opt",
+           "prefill_attn_gqa_varlen_opt", "prefill_attn_gqa_ring_opt",
            "prefill_attn_gqa_ring", "prefill_attn_gqa_decode", "prefill_attn_gqa_decode_opt",
            "pfa_decode_workspace_bytes", "pfa_status_str", "pfa_version")
 
@@ -76,6 +76,8 @@ def library() -> ctypes.CDLL:
         lib.pfa_decode_workspace_bytes.restype = ctypes.c_int64
         lib.prefill_attn_gqa_ring.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp, vp]
         lib.prefill_attn_gqa_ring.restype = ci
+        lib.prefill_attn_gqa_ring_opt.argtypes = lib.prefill_attn_gqa_ring.argtypes + [ctypes.POINTER(Options)]
+        lib.prefill_attn_gqa_ring_opt.restype = ci
         lib.pfa_status_str.argtypes = [ci]
         lib.pfa_status_str.restype = ctypes.c_char_p
         lib.pfa_version.argtypes = []
@@ -390,17 +392,25 @@ def prefill_attn_gqa_decode(q, k, v, *, scale: float | None = None, causal: bool
 
 def prefill_attn_gqa_ring_raw(q_ptr: int, kn_ptr: int, vn_ptr: int, kr_ptr: int, vr_ptr: int, B: int, Hq: int,
                               Hkv: int, L: int, pos0: int, ring: int, D: int, scale: float, window: int,
-                              o_ptr: int, stream: int | None) -> int:
+                              o_ptr: int, stream: int | None, flags: int = 0, softcap: float = 0.0,
+                              sinks_ptr: int | None = None) -> int:
     """Direct C-ABI call of the rotating-cache entry point; returns the status code."""
-    return int(library().prefill_attn_gqa_ring(q_ptr, kn_ptr, vn_ptr, kr_ptr, vr_ptr, B, Hq, Hkv, L, pos0, ring, D,
-                                               ctypes.c_float(scale), window, o_ptr, stream or None))
+    if flags == 0 and softcap == 0.0 and not sinks_ptr:
+        return int(library().prefill_attn_gqa_ring(q_ptr, kn_ptr, vn_ptr, kr_ptr, vr_ptr, B, Hq, Hkv, L, pos0, ring,
+                                                   D, ctypes.c_float(scale), window, o_ptr, stream or None))
+    opts = Options(flags, softcap, None, 0, 0, 0, sinks_ptr or None)
+    return int(library().prefill_attn_gqa_ring_opt(q_ptr, kn_ptr, vn_ptr, kr_ptr, vr_ptr, B, Hq, Hkv, L, pos0, ring,
+                                                   D, ctypes.c_float(scale), window, o_ptr, stream or None,
+                                                   ctypes.byref(opts)))
 
 
 def prefill_attn_gqa_ring(q, k_new, v_new, k_ring, v_ring, pos0: int, *, scale: float | None = None,
-                          window: int = 0, out=None, stream=None):
+                          window: int = 0, out=None, no_skip: bool = False, softcap: float = 0.0, sinks=None,
+                          stream=None):
     """Causal (optionally windowed) prefill of a chunk at positions pos0.. against a rotating cache,
     appending the chunk's keys first. q: bf16 [B,Hq,L,D]; k_new, v_new: bf16 [B,Hkv,L,D]; k_ring,
-    v_ring: bf16 [B,Hkv,ring,D] (position j in slot j % ring; updated in place). Returns `out`."""
+    v_ring: bf16 [B,Hkv,ring,D] (position j in slot j % ring; updated in place). no_skip, softcap and
+    sinks as in prefill_attn_gqa. Returns `out`."""
     import torch
 
     for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_ring", k_ring), ("v_ring", v_ring)):
@@ -428,7 +438,8 @@ def prefill_attn_gqa_ring(q, k_new, v_new, k_ring, v_ring, pos0: int, *, scale: 
     with torch.cuda.device(q.device):
         rc = prefill_attn_gqa_ring_raw(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_ring.data_ptr(),
                                        v_ring.data_ptr(), B, Hq, Hkv, L, int(pos0), ring, D, float(scale),
-                                       int(window), out.data_ptr(), stream_ptr)
+                                       int(window), out.data_ptr(), stream_ptr, FLAG_NO_SKIP if no_skip else 0,
+                                       float(softcap), _sinks_ptr(sinks, Hq, q.device))
     if rc != 0:
         raise PfaError(rc, status_str(rc))
     return out

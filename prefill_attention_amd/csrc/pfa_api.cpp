@@ -290,9 +290,9 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int L, int S, int D) {
 
 extern "C" {
 
-int prefill_attn_gqa_ring(const void* Q, const void* K_new, const void* V_new, void* K_ring, void* V_ring, int B,
-                          int Hq, int Hkv, int L, int pos0, int ring, int D, float scale, int window, void* O,
-                          void* stream) {
+int prefill_attn_gqa_ring_opt(const void* Q, const void* K_new, const void* V_new, void* K_ring, void* V_ring,
+                              int B, int Hq, int Hkv, int L, int pos0, int ring, int D, float scale, int window,
+                              void* O, void* stream, const pfa_options* opts) {
   if (!Q || !K_new || !V_new || !K_ring || !V_ring || !O) return PFA_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1 || pos0 < 0 || ring < 1) return PFA_ERR_SIZE;
   if (static_cast<long long>(pos0) + L > PFA_MAX_LEN || ring > PFA_MAX_LEN) return PFA_ERR_SIZE;
@@ -324,7 +324,16 @@ int prefill_attn_gqa_ring(const void* Q, const void* K_new, const void* V_new, v
       overlaps(rkr, rq) || overlaps(rkr, rkn) || overlaps(rkr, rvn) || overlaps(rkr, rvr) ||
       overlaps(rvr, rq) || overlaps(rvr, rkn) || overlaps(rvr, rvn))
     return PFA_ERR_ALIAS;
-  int rc = pfa::launch_ring_append(K_new, V_new, K_ring, V_ring, B, Hkv, L, D, ring, pos0, stream);
+  const unsigned flags = opts ? opts->flags : 0u;
+  const float softcap = opts ? opts->softcap : 0.0f;
+  if (flags & ~PFA_FLAG_NO_SKIP) return PFA_ERR_FLAGS;
+  if (!std::isfinite(softcap) || softcap < 0.0f) return PFA_ERR_SCALE;
+  // no additive bias and no block bitmap through the rotating cache
+  if (opts && (opts->bias || opts->block_sel)) return PFA_ERR_MASK_ARGS;
+  // the rings are written before the sink logits are read: they must not overlap (4 bytes = 2 elements per head)
+  if (opts && opts->sinks && (overlaps(rkr, at(opts->sinks, 2LL * Hq)) || overlaps(rvr, at(opts->sinks, 2LL * Hq))))
+    return PFA_ERR_ALIAS;
+  int rc = check_sinks(opts, Hq, ro);
   if (rc != PFA_OK) return rc;
   pfa::Launch p;
   p.q = Q;
@@ -343,11 +352,22 @@ int prefill_attn_gqa_ring(const void* Q, const void* K_new, const void* V_new, v
   p.causal = 1;
   p.causal_offset = pos0;
   p.window = window > 0 ? window : 0;
-  p.flags = 0;
+  p.flags = flags;
   p.stream = stream;
   p.ring = ring;
-  if (pfa::grid_blocks(p) > INT_MAX) return PFA_ERR_SIZE;
+  p.softcap = softcap;
+  p.sinks = opts ? opts->sinks : nullptr;
+  if (pfa::grid_blocks(p) > INT_MAX) return PFA_ERR_SIZE;  // checked before anything is enqueued
+  rc = pfa::launch_ring_append(K_new, V_new, K_ring, V_ring, B, Hkv, L, D, ring, pos0, stream);
+  if (rc != PFA_OK) return rc;
   return pfa::launch_prefill(p);
+}
+
+int prefill_attn_gqa_ring(const void* Q, const void* K_new, const void* V_new, void* K_ring, void* V_ring, int B,
+                          int Hq, int Hkv, int L, int pos0, int ring, int D, float scale, int window, void* O,
+                          void* stream) {
+  return prefill_attn_gqa_ring_opt(Q, K_new, V_new, K_ring, V_ring, B, Hq, Hkv, L, pos0, ring, D, scale, window, O,
+                                   stream, nullptr);
 }
 
 int64_t pfa_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D) {

@@ -396,3 +396,20 @@ def vocall(flags=0, softcap=0.0, sinks=None, bias=None, sel=None):
 ], ids=lambda x: str(x))
 def test_varlen_options_rejected(lib, kw, code):
     assert vocall(**kw) == code
+
+
+def rocall(flags=0, softcap=0.0, sinks=None, bias=None, sel=None):
+    a = dict(RGOOD)
+    opts = pfa.Options(flags, softcap, bias, 0, 0, 0, sinks, sel, 32 if sel else 0, 64 if sel else 0, 0, 0, 1)
+    return pfa.library().prefill_attn_gqa_ring_opt(
+        a["q"], a["kn"], a["vn"], a["kr"], a["vr"], a["B"], a["Hq"], a["Hkv"], a["L"], a["pos0"], a["ring"], a["D"],
+        ctypes.c_float(a["scale"]), a["window"], a["o"], None, ctypes.byref(opts))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=2), 9), (dict(softcap=-1.0), 6), (dict(bias=BIAS), 5), (dict(sel=SEL), 5),
+    (dict(sinks=SINKS + 2), 7), (dict(sinks=O + 4), 8),
+    (dict(sinks=KR + 64), 8), (dict(sinks=VR), 8),        # the rings are written before the sinks are read
+], ids=lambda x: str(x))
+def test_ring_options_rejected(lib, kw, code):
+    assert rocall(**kw) == code

@@ -106,3 +106,28 @@ def test_ring_too_small_raises_and_touches_nothing():
                                   dev_bf16(x["v_ring"]), 2000, window=1100)
     torch.cuda.synchronize()
     assert torch.equal(kr.view(torch.int16), before.view(torch.int16))
+
+
+@pytest.mark.parametrize("D,W", [(128, 1024), (64, 0)])
+def test_ring_options(D, W):
+    """Soft-cap and sinks through the rotating cache: bit-identical to the dense call with the same
+    options on the logical keys, skip == no-skip bit for bit, and within tolerance of the oracle."""
+    x = make_case(1, 8, 2, D, 200, 3000 if W else 400, 1280 if W else 640, W, seed=77)
+    sinks = (np.random.default_rng(78).standard_normal(8) * 2.0).astype(np.float32)
+    print(f"ring options D={D} W={W}", flush=True)
+    st = torch.from_numpy(sinks).to(DEV)
+    q = dev_bf16(x["q"])
+    outs = []
+    for no_skip in (False, True):
+        kr, vr = dev_bf16(x["k_ring"]), dev_bf16(x["v_ring"])
+        outs.append(pfa.prefill_attn_gqa_ring(q, dev_bf16(x["k_new"]), dev_bf16(x["v_new"]), kr, vr, x["pos0"],
+                                              scale=float(x["scale"]), window=W, softcap=6.0, sinks=st,
+                                              no_skip=no_skip))
+    dense = pfa.prefill_attn_gqa(q, dev_bf16(x["k_log"]), dev_bf16(x["v_log"]), scale=float(x["scale"]),
+                                 causal_offset=x["pos0"], window=W, softcap=6.0, sinks=st)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), dense.view(torch.int16))
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    ref = oracle_sdpa(x["q"], x["k_log"], x["v_log"], x["scale"], x["pos0"], W, None, workers=16, softcap=6.0,
+                      sinks=sinks.astype(np.float64))
+    check_close(outs[0].double().cpu().numpy(), ref, f"ring options D={D} W={W}")
