@@ -264,9 +264,13 @@ namespace pfa {
 
 DecodePlan decode_plan(int B, int Hq, int Hkv, int L, int S, int D) {
   // one round of single-wave workgroups (five fit a compute unit's LDS, 256 units), at least
-  // four 32-key tiles per split
+  // four 32-key tiles per split; with at most 32 rows per KV head (the register-K kernel, whose
+  // waves stream the keys fastest) at least twelve, which halves the partials the merge reads and
+  // still leaves about 700 workgroups for one-token decode on a 32K cache (15 % faster per call
+  // than four; the 64-row kernel needs the smaller splits to fill the chip)
   constexpr long long kTargetGroups = 1280;
   constexpr long long kMinTilesPerSplit = 4;
+  constexpr long long kMinTilesPerSplitFewRows = 12;
   DecodePlan pl;
   const long long R = static_cast<long long>(Hq / Hkv) * L;
   pl.n_rowgrp = static_cast<int>((R + 63) / 64);
@@ -278,6 +282,7 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int L, int S, int D) {
   if (n_split < 1) n_split = 1;
   long long tps = (tiles + n_split - 1) / n_split;
   if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
+  if (pl.rows_cap <= 32 && tps < kMinTilesPerSplitFewRows) tps = kMinTilesPerSplitFewRows;
   n_split = (tiles + tps - 1) / tps;
   pl.n_split = static_cast<int>(n_split);
   pl.tiles_per_split = static_cast<int>(tps);
