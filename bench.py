@@ -1,6 +1,7 @@
 """Throughput of grouped-query flash prefill attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--cold-mib N]
     python bench.py --calibrate-copy     (three plain 1 GiB device copies: the reference kernel
                                           that HBM byte counters are scaled against)
 
@@ -13,6 +14,13 @@ value = useful TFLOP/s = 4 * D * (visible query-key pairs) / time, whole job.
 roofline: the prefill kernel against the bf16 dense MFMA peak, with its average launch duration
 taken from HIP events recorded on the launch stream around every launch of the timed region.
 cpu_baseline: the fp64 CPU oracle, timed on a bounded sample of the same workload.
+--cold-mib N: every launch reads a different copy of its inputs (and writes a different output),
+cycling through enough copies to exceed N MiB, so that no launch finds its operands in the L2 or the
+256 MB last-level (MALL) cache; 0 reuses the same buffers (warm). Workloads whose arithmetic
+intensity is below the ridge (bf16 peak / HBM peak, about 315 flop/byte: decode, small prompts) are
+HBM-bound: they default to cold (512 MiB; a one-token call on a 32K cache reads 134 MB, which the
+last-level cache would otherwise serve in part) and report their roofline against HBM bandwidth with
+algorithmic bytes; the others default to warm and report against the MFMA peak.
 """
 from __future__ import annotations
 
@@ -73,6 +81,18 @@ def visible_pairs(c: dict, key_lengths=None) -> int:
         lo = max(0, i + off - W + 1) if W > 0 else 0
         total += max(0, hi - lo + 1)
     return B * Hq * total
+
+
+def below_ridge(workload: str) -> bool:
+    """Whether the workload's useful flops per algorithmic byte fall below the bf16-MFMA / HBM ridge
+    (key-padded chunks counted at full length: an upper bound on their flops)."""
+    from workloads import CONFIGS
+
+    names = [n for n in WORKLOADS[workload] if n in CONFIGS]
+    if len(names) != len(WORKLOADS[workload]):
+        return False  # packed varlen batches: long causal prompts, far above the ridge
+    flops = sum(4 * CONFIGS[n]["D"] * visible_pairs(CONFIGS[n]) for n in names)
+    return flops / sum(algorithmic_bytes(CONFIGS[n]) for n in names) < PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3
 
 
 def sel_visible_pairs(c: dict, block_sel, block_q: int, block_k: int) -> int:
@@ -252,6 +272,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--cold-mib", type=int, default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this prefill-attention library has no multi-GPU path "
@@ -278,6 +299,9 @@ def main() -> int:
     calls = []
     total_flops = 0
     per_cfg = []
+    cold_copies = {}
+    if args.cold_mib is None:
+        args.cold_mib = 512 if below_ridge(args.workload) else 0
     def t(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
@@ -329,6 +353,21 @@ def main() -> int:
 
         def launch(q=q, k=k, v=v, kw=kw, fn=fn):
             fn(q, k, v, **kw)
+
+        if args.cold_mib > 0 and c.get("entry") != "ring":
+            # rotating copies: one (q, k, v, out, key mask) set per launch, cycled
+            per_copy = (q.numel() + k.numel() + v.numel() + out.numel()) * 2 + (m.numel() if m is not None else 0)
+            n_copies = max(2, -(-args.cold_mib * 2 ** 20 // per_copy))
+            sets = [(q, k, v, out, m)] + [(q.clone(), k.clone(), v.clone(), torch.empty_like(out),
+                                          m.clone() if m is not None else None) for _ in range(n_copies - 1)]
+            turn = [0]
+
+            def launch(sets=sets, kw=kw, fn=fn, turn=turn):
+                qq, kk, vv, oo, mm = sets[turn[0]]
+                turn[0] = (turn[0] + 1) % len(sets)
+                fn(qq, kk, vv, **(kw | dict(out=oo, key_mask=mm)))
+
+            cold_copies[name] = n_copies
 
         if c.get("entry") == "ring":
             pos0, ring = c["causal_offset"], c["ring"]
@@ -396,6 +435,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload,
                    "description": DESCRIPTION.get(args.workload, args.workload),
+                   "caches": (f"cold: each launch reads one of {cold_copies} copies of its inputs "
+                              f"(> {args.cold_mib} MiB per chunk)") if cold_copies else "warm: inputs reused",
                    "chunks": [(CONFIGS.get(n) or VARLEN_CONFIGS[n]) | {"name": n} for n in WORKLOADS[args.workload]]},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "per_workload": [{
@@ -418,9 +459,10 @@ def main() -> int:
             "useful_flops_per_launch": total_flops / len(calls),
         },
     }
-    if all(CONFIGS.get(n, {}).get("entry") == "decode" for n in WORKLOADS[args.workload]):
-        # short-query launches read each KV head's keys once for a few rows: far below the ridge,
-        # bound by HBM. The launch time covers both kernels of the call (split and merge).
+    intensity = total_flops / sum(pc["bytes"] for pc in per_cfg)
+    if intensity < PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
+        # below the ridge (short queries: decode, small prompts): bound by HBM. A decode call's
+        # launch time covers both of its kernels (split and merge).
         alg_bytes = sum(pc["bytes"] for pc in per_cfg) / len(calls)
         gbs = alg_bytes / (kernel_ms_total / len(calls) * 1e-3) / 1e9
         rec["roofline"] = {
