@@ -51,9 +51,10 @@ def check_close(got, ref, what=""):
 
 
 # ragged length sets: single rows, tails, several key tiles, a sequence without rows, one with
-# more rows than keys, one longer than a 256-row workgroup
+# more rows than keys, one longer than a 256-row workgroup, sequences with rows but no keys
 LENGTHS = {
     "ragged": ([1, 33, 300, 0, 517, 64], [1, 40, 300, 10, 1100, 764]),
+    "no_keys": ([3, 40, 7, 1], [0, 64, 0, 1]),
     "equal": ([5, 129, 256, 257, 90], [5, 129, 256, 257, 90]),
     "short_keys": ([200, 70], [37, 70]),
 }
@@ -69,10 +70,12 @@ def test_varlen_parity(D, lengths, causal, window):
     got = run_varlen(x, causal=causal, window=window).double().cpu().numpy()
     ref = oracle_varlen(x["q"], x["k"], x["v"], x["cu_q"], x["cu_k"], x["scale"], causal, window)
     check_close(got, ref, f"D={D} {lengths} causal={causal} W={window}")
-    # rows that see no key are exact zeros
+    # rows that see no key are exact zeros (every row of a sequence without keys)
     for b in range(len(lq)):
-        if causal and lq[b] > lk[b]:
-            s0 = int(x["cu_q"][b])
+        s0 = int(x["cu_q"][b])
+        if lk[b] == 0:
+            assert torch.count_nonzero(torch.from_numpy(got[s0:s0 + lq[b]])) == 0
+        elif causal and lq[b] > lk[b]:
             assert torch.count_nonzero(torch.from_numpy(got[s0:s0 + lq[b] - lk[b]])) == 0
 
 
