@@ -62,6 +62,9 @@ CASES = [
     ("l8_g4_rows32_window", 2, 16, 4, 128, 8, 1000, 992, 300, None),
     # one tile per split and keys shorter than a tile for some rows (padding steps of the split kernel)
     ("l2_g2_s70", 3, 4, 2, 128, 2, 70, 68, 0, None),
+    # one visible key per row (window 1): the output is that key's value row, bit for bit
+    ("l4_window1", 2, 8, 2, 128, 4, 300, 296, 1, None),
+    ("l40_window1_rows160", 1, 16, 4, 64, 40, 1000, 960, 1, None),
 ]
 
 
@@ -77,6 +80,13 @@ def test_decode_parity(case):
     # rows that see no key are exact zeros
     empty = ~np.any(np.abs(ref) > 0, axis=-1)
     assert np.all(got[empty] == 0.0)
+    if W == 1:  # row i sees only key i + off: P = 1, l = 1, and O is that value row exactly
+        G = Hq // Hkv
+        vbits = x["v"]
+        for h in range(Hq):
+            want = vbits[:, h // G, off:off + L, :]
+            gotbits = torch.from_numpy(got[:, h].astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+            assert np.array_equal(gotbits.view(np.uint16), want.view(np.uint16)), f"{name}: head {h}"
 
 
 def test_decode_deterministic_and_workspace_reuse():
