@@ -81,3 +81,108 @@ def test_random_shape(i):
     assert np.all(got[empty] == 0.0), msg
     if c["entry"] == "prefill":
         assert torch.equal(out.view(torch.int16), out_ns.view(torch.int16)), f"skip != no-skip: {msg}"
+
+
+# ---- packed variable-length batches ----
+
+N_VARLEN = 24
+
+
+def check(got, ref, msg):
+    err = np.abs(got - ref)
+    bad = err > ATOL + RTOL * np.abs(ref)
+    rms_ref = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    rms_err = float(np.sqrt(np.mean(err ** 2))) if ref.size else 0.0
+    full = f"{msg}: max_abs={err.max(initial=0):.3e} rms_err={rms_err:.3e} rms_ref={rms_ref:.3e} bad={int(bad.sum())}"
+    assert not bad.any(), full
+    if rms_ref > 0:
+        assert rms_err <= RMS_RATIO * rms_ref, full
+    empty = ~np.any(np.abs(ref) > 0, axis=-1)
+    assert np.all(got[empty] == 0.0), full
+
+
+def draw_varlen(i):
+    r = np.random.default_rng(3000 + i)
+    n = int(r.integers(1, 7))
+    causal = bool(r.random() < 0.75)
+    lq = r.integers(0, 301, size=n)
+    lq[int(r.integers(0, n))] = max(1, int(lq.max()))  # at least one row in the batch
+    lk = lq + r.integers(0, 301, size=n) if causal else r.integers(0, 401, size=n)
+    lk[int(r.integers(0, n))] = max(1, int(lk.max()))  # at least one key in the batch
+    Hkv = int(r.integers(1, 3))
+    return dict(n_seq=n, Hq=Hkv * int(r.choice([1, 2, 4])), Hkv=Hkv, D=int(r.choice([64, 128])), lq=(0, 0),
+                prefix=(0, 0), causal=causal, window=int(r.integers(1, 400)) if causal and r.random() < 0.35 else 0,
+                lengths_q=[int(t) for t in lq], lengths_k=[int(t) for t in lk],
+                softcap=float(r.choice([0.0, 0.0, 20.0])), sinks=bool(r.random() < 0.3))
+
+
+@pytest.mark.parametrize("i", range(N_VARLEN))
+def test_random_varlen(i):
+    from oracle.varlen import oracle_varlen
+    from workloads import make_varlen_inputs
+
+    c = draw_varlen(i)
+    print(f"random varlen case {i}: {c}", flush=True)
+    x = make_varlen_inputs({k: c[k] for k in ("n_seq", "Hq", "Hkv", "D", "lq", "prefix", "causal", "window")},
+                           seed=4000 + i, lengths_q=c["lengths_q"], lengths_k=c["lengths_k"])
+    sinks = np.random.default_rng(5000 + i).standard_normal(c["Hq"], dtype=np.float32) if c["sinks"] else None
+    q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    cq = torch.from_numpy(x["cu_q"]).to(DEV)
+    ck = torch.from_numpy(x["cu_k"]).to(DEV)
+    kw = dict(scale=float(x["scale"]), causal=x["causal"], window=x["window"], softcap=c["softcap"],
+              sinks=torch.from_numpy(sinks).to(DEV) if sinks is not None else None)
+    out = pfa.prefill_attn_gqa_varlen(q, k, v, cq, ck, x["max_seqlen_q"], **kw)
+    out_ns = pfa.prefill_attn_gqa_varlen(q, k, v, cq, ck, x["max_seqlen_q"], no_skip=True, **kw)
+    torch.cuda.synchronize()
+    ref = oracle_varlen(x["q"], x["k"], x["v"], x["cu_q"], x["cu_k"], x["scale"], x["causal"], x["window"],
+                        softcap=c["softcap"], sinks=sinks)
+    check(out.double().cpu().numpy(), ref, f"varlen case {i} {c}")
+    assert torch.equal(out.view(torch.int16), out_ns.view(torch.int16)), f"varlen case {i}: skip != no-skip"
+
+
+# ---- rotating cache ----
+
+N_RING = 24
+
+
+def draw_ring(i):
+    r = np.random.default_rng(6000 + i)
+    L = int(r.integers(1, 201))
+    pos0 = int(r.choice([0, int(r.integers(0, 200)), int(r.integers(0, 3001))]))
+    W = int(r.integers(1, 601)) if r.random() < 0.6 else 0
+    need = min(W - 1 + L, pos0 + L) if W > 0 else pos0 + L
+    ring = max(64, need + int(r.choice([0, 0, int(r.integers(1, 100))])))
+    Hkv = int(r.integers(1, 3))
+    return dict(B=int(r.integers(1, 3)), Hq=Hkv * int(r.choice([1, 2, 4])), Hkv=Hkv, D=int(r.choice([64, 128])),
+                L=L, pos0=pos0, W=W, ring=ring, softcap=float(r.choice([0.0, 0.0, 20.0])),
+                sinks=bool(r.random() < 0.3))
+
+
+@pytest.mark.parametrize("i", range(N_RING))
+def test_random_ring(i):
+    from workloads import random_bits
+
+    c = draw_ring(i)
+    print(f"random ring case {i}: {c}", flush=True)
+    B, Hq, Hkv, D, L, pos0, W, ring = (c[k] for k in ("B", "Hq", "Hkv", "D", "L", "pos0", "W", "ring"))
+    rng = np.random.default_rng(7000 + i)
+    q = random_bits(rng, (B, Hq, L, D))
+    k_log = random_bits(rng, (B, Hkv, pos0 + L, D))
+    v_log = random_bits(rng, (B, Hkv, pos0 + L, D))
+    k_ring = random_bits(rng, (B, Hkv, ring, D), amp=4.0)  # stale slots: values no row may see
+    v_ring = random_bits(rng, (B, Hkv, ring, D), amp=4.0)
+    for p in range(max(0, pos0 - ring), pos0):
+        k_ring[:, :, p % ring] = k_log[:, :, p]
+        v_ring[:, :, p % ring] = v_log[:, :, p]
+    sinks = rng.standard_normal(Hq, dtype=np.float32) if c["sinks"] else None
+    scale = np.float32(1.0 / np.sqrt(np.float32(D)))
+    opts = dict(softcap=c["softcap"], sinks=torch.from_numpy(sinks).to(DEV) if sinks is not None else None)
+    qd = dev_bf16(q)
+    out = pfa.prefill_attn_gqa_ring(qd, dev_bf16(k_log[:, :, pos0:]), dev_bf16(v_log[:, :, pos0:]), dev_bf16(k_ring),
+                                    dev_bf16(v_ring), pos0, scale=float(scale), window=W, **opts)
+    dense = pfa.prefill_attn_gqa(qd, dev_bf16(k_log), dev_bf16(v_log), scale=float(scale), causal_offset=pos0,
+                                 window=W, **opts)
+    torch.cuda.synchronize()
+    ref = oracle_sdpa(q, k_log, v_log, scale, pos0, W, None, workers=16, softcap=c["softcap"], sinks=sinks)
+    check(out.double().cpu().numpy(), ref, f"ring case {i} {c}")
+    assert torch.equal(out.view(torch.int16), dense.view(torch.int16)), f"ring case {i}: ring != dense on the logical keys"
