@@ -186,3 +186,64 @@ def test_random_ring(i):
     ref = oracle_sdpa(q, k_log, v_log, scale, pos0, W, None, workers=16, softcap=c["softcap"], sinks=sinks)
     check(out.double().cpu().numpy(), ref, f"ring case {i} {c}")
     assert torch.equal(out.view(torch.int16), dense.view(torch.int16)), f"ring case {i}: ring != dense on the logical keys"
+
+
+# ---- dense-only options: additive bias, block bitmap ----
+
+N_OPT = 24
+
+
+def draw_opt(i):
+    r = np.random.default_rng(8000 + i)
+    L, S = int(r.integers(1, 301)), int(r.integers(1, 601))
+    Hkv = int(r.integers(1, 3))
+    off = NO_CAUSAL if r.random() < 0.2 else int(r.choice([0, max(0, S - L), int(r.integers(0, S + 40))]))
+    W = int(r.integers(1, S + 2)) if off >= 0 and r.random() < 0.35 else 0
+    return dict(B=int(r.integers(1, 3)), Hq=Hkv * int(r.choice([1, 2, 4])), Hkv=Hkv, D=int(r.choice([64, 128])),
+                L=L, S=S, causal_offset=off, window=W, amp=1.0, key_padding=None,
+                softcap=float(r.choice([0.0, 0.0, 20.0])), sinks=bool(r.random() < 0.3),
+                kind="bias" if i % 2 == 0 else "sel",
+                bias_shape=int(r.integers(0, 5)), sel_shape=int(r.integers(0, 3)),
+                block_q=int(r.choice([32, 64, 96, 128, 256])), block_k=int(r.choice([64, 128, 192, 320])),
+                density=float(r.uniform(0.2, 0.8)))
+
+
+@pytest.mark.parametrize("i", range(N_OPT))
+def test_random_bias_and_bitmap(i):
+    c = draw_opt(i)
+    print(f"random option case {i}: {c}", flush=True)
+    x = make_inputs({k: c[k] for k in ("B", "Hq", "Hkv", "D", "L", "S", "causal_offset", "window", "amp",
+                                       "key_padding", "sinks")}, seed=9000 + i)
+    B, Hq, L, S = c["B"], c["Hq"], c["L"], c["S"]
+    r = np.random.default_rng(9500 + i)
+    q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    sinks = x["sinks"]
+    off, W = x["causal_offset"], x["window"]
+    kw = dict(scale=float(x["scale"]), causal=off >= 0, causal_offset=off if off >= 0 else None, window=W,
+              softcap=c["softcap"], sinks=torch.from_numpy(sinks).to(DEV) if sinks is not None else None)
+    ref_kw = {}
+    if c["kind"] == "bias":
+        # one of [L,S], [1,Hq,L,S], [B,1,L,S], [B,Hq,L,S], [1,1,1,S]; about 10 % of entries -inf; the key
+        # dimension padded to a multiple of 4 elements (the row stride the library requires)
+        shape = [(1, 1, L, S), (1, Hq, L, S), (B, 1, L, S), (B, Hq, L, S), (1, 1, 1, S)][c["bias_shape"]]
+        vals = (r.standard_normal(shape, dtype=np.float32) * np.float32(2.0))
+        vals[r.random(shape) < 0.1] = -np.inf
+        S4 = -(-S // 4) * 4
+        buf = torch.zeros(shape[:3] + (S4,), dtype=torch.float32, device=DEV)
+        buf[..., :S] = torch.from_numpy(vals).to(DEV)
+        kw["bias"] = buf[..., :S] if c["bias_shape"] != 0 else buf[0, 0, :, :S]
+        ref_kw["bias"] = vals
+    else:
+        bq, bk = c["block_q"], c["block_k"]
+        nqb, nkb = -(-L // bq), -(-S // bk)
+        shape = [(nqb, nkb), (Hq, nqb, nkb), (B, Hq, nqb, nkb)][c["sel_shape"]]
+        sel = (r.random(shape) < c["density"]).astype(np.uint8)
+        kw.update(block_sel=torch.from_numpy(sel).to(DEV), block_q=bq, block_k=bk)
+        ref_kw.update(block_sel=sel, block_q=bq, block_k=bk)
+    out = pfa.prefill_attn_gqa(q, k, v, **kw)
+    out_ns = pfa.prefill_attn_gqa(q, k, v, no_skip=True, **kw)
+    torch.cuda.synchronize()
+    ref = oracle_sdpa(x["q"], x["k"], x["v"], x["scale"], off, W, None, workers=16, softcap=c["softcap"],
+                      sinks=sinks, **ref_kw)
+    check(out.double().cpu().numpy(), ref, f"option case {i} {c}")
+    assert torch.equal(out.view(torch.int16), out_ns.view(torch.int16)), f"option case {i}: skip != no-skip"
