@@ -14,9 +14,10 @@ value = useful TFLOP/s = 4 * D * (visible query-key pairs) / time, whole job.
 roofline: the prefill kernel against the bf16 dense MFMA peak, with its average launch duration
 taken from HIP events recorded on the launch stream around every launch of the timed region.
 cpu_baseline: the fp64 CPU oracle, timed on a bounded sample of the same workload.
---cold-mib N: every launch reads a different copy of its inputs (and writes a different output),
-cycling through enough copies to exceed N MiB, so that no launch finds its operands in the L2 or the
-256 MB last-level (MALL) cache; 0 reuses the same buffers (warm). Workloads whose arithmetic
+--cold-mib N: every launch reads a different copy of Q, K, V and the key mask (and writes a different
+O), cycling through enough copies to exceed N MiB, so that no launch finds its operands in the L2 or
+the 256 MB last-level (MALL) cache; 0 reuses the same buffers (warm). Bias, sinks and bitmaps are
+shared by the copies, and the rotating-cache workload always reuses its cache. Workloads whose arithmetic
 intensity is below the ridge (bf16 peak / HBM peak, about 315 flop/byte: decode, small prompts) are
 HBM-bound: they default to cold (512 MiB; a one-token call on a 32K cache reads 134 MB, which the
 last-level cache would otherwise serve in part) and report their roofline against HBM bandwidth with
