@@ -164,6 +164,26 @@ def recorded_traffic(workload: str):
     return float(val.group(1))
 
 
+def cgroup_cpu_quota():
+    """Whole cores granted by the cgroup CPU quota (cgroup v2 cpu.max or v1 cfs files), or None."""
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            return max(1, int(int(quota) // int(period)))
+        return None
+    except (OSError, ValueError):
+        pass
+    try:
+        with open("/sys/fs/cgroup/cpu/cpu.cfs_quota_us") as f:
+            quota = int(f.read())
+        with open("/sys/fs/cgroup/cpu/cpu.cfs_period_us") as f:
+            period = int(f.read())
+        return max(1, quota // period) if quota > 0 else None
+    except (OSError, ValueError):
+        return None
+
+
 def blas_single_thread():
     """Context that pins the BLAS library to one thread per calling thread, so that `cores` is the
     number of worker threads actually used."""
@@ -493,11 +513,17 @@ def main() -> int:
         }
     if not args.no_cpu_baseline:
         from oracle import host_workers
-        workers = min(16, host_workers())
+        affinity = host_workers()
+        quota = cgroup_cpu_quota()
+        # one oracle thread per core this process may actually run on: the affinity mask, bounded by
+        # the cgroup CPU quota when one is set (threads beyond the quota only time-share it)
+        workers = max(1, min(affinity, quota)) if quota else affinity
         if args.workload == "varlen_causal_b8":
             rec["cpu_baseline"] = varlen_cpu_baseline(args.workload, workers, args.cpu_budget)
         else:
             rec["cpu_baseline"] = cpu_baseline(args.workload, workers, args.cpu_budget)
+        rec["cpu_baseline"]["affinity_cores"] = affinity
+        rec["cpu_baseline"]["cpu_quota_cores"] = quota
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define PFA_VERSION 10600 /* 1.6.0 */
+#define PFA_VERSION 10700 /* 1.7.0 */
 
 /* causal_offset < 0 selects bidirectional attention (no causal term). */
 #define PFA_NO_CAUSAL (-1)
@@ -60,18 +60,23 @@ extern "C" {
 /* Largest L accepted by the short-query (decode) entry point. */
 #define PFA_DECODE_MAX_L 64
 
+/* Status codes. Codes 0-8 are the base set in their base order; 9-12 were added for the flags,
+ * the scale check, the decode workspace and the rotating cache. Validation runs in the order
+ * NULL, SIZE, GQA, HEAD_DIM, MASK_ARGS, SCALE, ALIGN, ALIAS, FLAGS (the first failing check is
+ * returned); LAUNCH can only follow a call that passed all of them. */
 enum pfa_status {
   PFA_OK = 0,
   PFA_ERR_NULL = 1,      /* Q, K, V, O, a varlen prefix-sum buffer or the decode workspace NULL */
-  PFA_ERR_SIZE = 2,      /* a size < 1, L or S > PFA_MAX_LEN, or a size product / grid too big  */
+  PFA_ERR_SIZE = 2,      /* a size < 1, L or S > PFA_MAX_LEN, a size product / grid too big, or */
+                         /* one (b, KV head) ring of the rotating cache >= 2^31 bytes           */
   PFA_ERR_GQA = 3,       /* Hq is not a multiple of Hkv                                         */
   PFA_ERR_HEAD_DIM = 4,  /* D is not 64 or 128                                                  */
   PFA_ERR_MASK_ARGS = 5, /* window > 0 without the causal term; an unsupported mask combination */
-  PFA_ERR_SCALE = 6,     /* scale not finite or not > 0; softcap not finite or < 0              */
-  PFA_ERR_ALIGN = 7,     /* Q, K, V or O not 16-byte aligned (prefix sums: not 4-byte aligned)  */
-  PFA_ERR_ALIAS = 8,     /* O (or the decode workspace) overlaps another buffer of the call     */
+  PFA_ERR_ALIGN = 6,     /* Q, K, V or O not 16-byte aligned (prefix sums: not 4-byte aligned)  */
+  PFA_ERR_ALIAS = 7,     /* O (or the decode workspace) overlaps another buffer of the call     */
+  PFA_ERR_LAUNCH = 8,    /* the HIP launch failed (e.g. no gfx950 device is current)            */
   PFA_ERR_FLAGS = 9,     /* unknown bit in flags                                                */
-  PFA_ERR_LAUNCH = 10,   /* the HIP launch failed (e.g. no gfx950 device is current)            */
+  PFA_ERR_SCALE = 10,    /* scale not finite or not > 0; softcap not finite or < 0              */
   PFA_ERR_WORKSPACE = 11, /* decode workspace smaller than pfa_decode_workspace_bytes()         */
   PFA_ERR_RING = 12       /* ring cache smaller than 64 slots or than the keys the chunk sees   */
 };
@@ -232,7 +237,8 @@ int prefill_attn_gqa_varlen_opt(const void* Q, const void* K, const void* V,
  *   pos0          position of the chunk's first row (>= 0)
  *   ring          slots of the cache; >= 64 and >= min(window - 1 + L, pos0 + L) (with a window)
  *                 or >= pos0 + L (without one), so that appending the chunk overwrites no key a
- *                 row still sees
+ *                 row still sees (PFA_ERR_RING otherwise); ring * D * 2 < 2^31, i.e. one
+ *                 (b, KV head) ring under 2 GiB (PFA_ERR_SIZE otherwise: slot offsets are 32-bit)
  *   window        > 0: row at position p sees keys [max(0, p - window + 1), p]; <= 0: all of [0, p]
  *   O             bf16 [B, Hq, L, D], fully overwritten
  *

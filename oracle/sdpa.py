@@ -215,30 +215,48 @@ def oracle_sdpa(q, k, v, scale, causal_offset: int = NO_CAUSAL, window: int = 0,
     return out
 
 
+def key_valid_of(key_mask: np.ndarray | None, b: int) -> np.ndarray | None:
+    """The key-padding row of batch element b (brotensor key mask: nonzero = valid), or None."""
+    return None if key_mask is None else (np.asarray(key_mask)[b] != 0)
+
+
+def bias_of_row(bias: np.ndarray, shape: tuple, b: int, h: int, i: int) -> np.ndarray:
+    """fp64 [1, S]: the additive bias of query row i of (b, h), with `bias` broadcast (numpy rules)
+    to shape = (B, Hq, L, S) (tiny-llm Task 2: the additive mask broadcasts over batch and heads)."""
+    full = np.broadcast_to(np.asarray(bias, dtype=np.float64), shape)
+    return full[b, h, i:i + 1]
+
+
+def sel_of_row(block_sel: np.ndarray, shape: tuple, block_q: int, block_k: int, b: int, h: int,
+               i: int) -> np.ndarray:
+    """Boolean [1, S]: the block-bitmap selection of query row i of (b, h), with `block_sel`
+    broadcast to (B, Hq, ceil(L / block_q), ceil(S / block_k)); shape = (B, Hq, L, S)."""
+    B, Hq, L, S = shape
+    full = np.broadcast_to(np.asarray(block_sel), (B, Hq, -(-L // block_q), -(-S // block_k)))
+    return block_selected(np.array([i]), S, full[b, h], block_q, block_k)
+
+
 def oracle_selected_rows(q, k, v, scale, causal_offset, window, key_mask, picks,
                          softcap: float = 0.0, bias: np.ndarray | None = None,
                          sinks: np.ndarray | None = None, block_sel: np.ndarray | None = None,
                          block_q: int = 0, block_k: int = 0) -> np.ndarray:
     """Oracle output for selected (b, h, row) triples only: returns fp64 [len(picks), D].
 
-    Used at full workload sizes, where computing every row would take too long."""
-    Hq, Hkv = q.shape[1], k.shape[1]
-    L, S = q.shape[2], k.shape[2]
-    if block_sel is not None:
-        block_sel = np.broadcast_to(np.asarray(block_sel), (q.shape[0], Hq, -(-L // block_q), -(-S // block_k)))
+    The same definition as oracle_sdpa, one row at a time (used at full workload sizes, where
+    computing every row would take too long); each option is looked up for the picked row by
+    key_valid_of, bias_of_row and sel_of_row."""
+    B, Hq, L = q.shape[0], q.shape[1], q.shape[2]
+    Hkv, S = k.shape[1], k.shape[2]
+    shape = (B, Hq, L, S)
     res = []
     for (b, h, i) in picks:
         hk = kv_head_of(h, Hq, Hkv)
         kb, vb = _widen(k[b, hk]), _widen(v[b, hk])
         qr = _widen(q[b, h, i:i + 1])
-        kv = None if key_mask is None else (key_mask[b] != 0)
-        br = None
-        if bias is not None:
-            bfull = np.broadcast_to(np.asarray(bias, dtype=np.float64), (q.shape[0], Hq, q.shape[2], k.shape[2]))
-            br = bfull[b, h, i:i + 1]
-        sel = None if block_sel is None else block_selected(np.array([i]), S, block_sel[b, h], block_q, block_k)
+        br = None if bias is None else bias_of_row(bias, shape, b, h, i)
+        sel = None if block_sel is None else sel_of_row(block_sel, shape, block_q, block_k, b, h, i)
         res.append(attention_rows(qr, kb, vb, np.array([i]), float(np.float64(scale)),
-                                  causal_offset, window, kv, softcap, br,
+                                  causal_offset, window, key_valid_of(key_mask, b), softcap, br,
                                   None if sinks is None else float(np.float64(sinks[h])), sel)[0])
     return np.array(res)
 

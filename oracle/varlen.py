@@ -19,6 +19,8 @@ The logit soft-cap and the attention sinks are those of ``oracle.sdpa`` (same fu
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from .sdpa import _softmax_rows_times_v, _widen, kv_head_of, soft_cap
@@ -38,10 +40,11 @@ def varlen_visible(Lq: int, Lk: int, causal: bool, window: int) -> np.ndarray:
 
 
 def oracle_varlen(q, k, v, cu_q, cu_k, scale, causal: bool = True, window: int = 0, softcap: float = 0.0,
-                  sinks=None) -> np.ndarray:
+                  sinks=None, workers: int = 1) -> np.ndarray:
     """Packed variable-length SDPA in fp64. q: [total_q, Hq, D], k/v: [total_k, Hkv, D] as bf16 bits
     (uint16) or floats; cu_q / cu_k: prefix sums of n_seq + 1 entries; softcap > 0: logit soft-cap;
-    sinks: [Hq] sink logits or None. Returns fp64 [total_q, Hq, D]."""
+    sinks: [Hq] sink logits or None. Returns fp64 [total_q, Hq, D]. `workers` > 1 spreads the
+    (sequence, head) items over a thread pool (numpy releases the GIL)."""
     q, k, v = _widen(q), _widen(k), _widen(v)
     total_q, Hq, D = q.shape
     Hkv = k.shape[1]
@@ -53,32 +56,46 @@ def oracle_varlen(q, k, v, cu_q, cu_k, scale, causal: bool = True, window: int =
     cu_k = np.asarray(cu_k, dtype=np.int64)
     out = np.zeros((total_q, Hq, v.shape[-1]), dtype=np.float64)
     scale = float(np.float64(scale))
-    for b in range(len(cu_q) - 1):
+    def run(item):
+        b, h = item
         q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
         Lq, Lk = int(q1 - q0), int(k1 - k0)
-        if Lq == 0:
-            continue
+        if Lq == 0 or Lk == 0:
+            return  # no rows, or no keys: zeros
         add = np.where(varlen_visible(Lq, Lk, causal, window), 0.0, -np.inf)
-        for h in range(Hq):
-            hk = kv_head_of(h, Hq, Hkv)
-            if Lk == 0:
-                continue  # no keys: zeros
-            scores = soft_cap(scale * (q[q0:q1, h] @ k[k0:k1, hk].T), float(softcap)) + add
-            out[q0:q1, h] = _softmax_rows_times_v(scores, v[k0:k1, hk],
-                                                  None if sinks is None else float(np.float64(sinks[h])))
+        hk = kv_head_of(h, Hq, Hkv)
+        scores = soft_cap(scale * (q[q0:q1, h] @ k[k0:k1, hk].T), float(softcap)) + add
+        out[q0:q1, h] = _softmax_rows_times_v(scores, v[k0:k1, hk],
+                                              None if sinks is None else float(np.float64(sinks[h])))
+
+    items = [(b, h) for b in range(len(cu_q) - 1) for h in range(Hq)]
+    if workers <= 1:
+        for it in items:
+            run(it)
+    else:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(run, items))
     return out
+
+
+def sequence_of_row(cu_q, r: int) -> int:
+    """Index b of the sequence that owns packed query row r, i.e. cu_q[b] <= r < cu_q[b + 1]
+    (brotensor varlen layout). A sequence without rows owns none, so among equal prefix sums the
+    last one is the owner: the rightmost b with cu_q[b] <= r."""
+    return int(np.searchsorted(np.asarray(cu_q, dtype=np.int64), r, side="right") - 1)
 
 
 def oracle_varlen_rows(q, k, v, cu_q, cu_k, scale, causal, window, picks, softcap: float = 0.0,
                        sinks=None) -> np.ndarray:
-    """Oracle output for selected (packed row, query head) pairs only: fp64 [len(picks), D]. Used at
-    full workload sizes, where every row would take too long."""
+    """Oracle output for selected (packed row, query head) pairs only: fp64 [len(picks), D]. The
+    same definition as oracle_varlen, one row at a time (used at full workload sizes, where every
+    row would take too long); the row's sequence comes from sequence_of_row."""
     Hq, Hkv = q.shape[1], k.shape[1]
     cu_q = np.asarray(cu_q, dtype=np.int64)
     cu_k = np.asarray(cu_k, dtype=np.int64)
     res = []
     for (r, h) in picks:
-        b = int(np.searchsorted(cu_q, r, side="right") - 1)
+        b = sequence_of_row(cu_q, r)
         q0, k0, k1 = cu_q[b], cu_k[b], cu_k[b + 1]
         Lq, Lk = int(cu_q[b + 1] - q0), int(k1 - k0)
         i = int(r - q0)

@@ -19,8 +19,8 @@ FLAG_NO_SKIP = 1
 MAX_LEN = 1 << 30
 STATUS = {
     0: "PFA_OK", 1: "PFA_ERR_NULL", 2: "PFA_ERR_SIZE", 3: "PFA_ERR_GQA", 4: "PFA_ERR_HEAD_DIM",
-    5: "PFA_ERR_MASK_ARGS", 6: "PFA_ERR_SCALE", 7: "PFA_ERR_ALIGN", 8: "PFA_ERR_ALIAS",
-    9: "PFA_ERR_FLAGS", 10: "PFA_ERR_LAUNCH", 11: "PFA_ERR_WORKSPACE", 12: "PFA_ERR_RING",
+    5: "PFA_ERR_MASK_ARGS", 6: "PFA_ERR_ALIGN", 7: "PFA_ERR_ALIAS", 8: "PFA_ERR_LAUNCH",
+    9: "PFA_ERR_FLAGS", 10: "PFA_ERR_SCALE", 11: "PFA_ERR_WORKSPACE", 12: "PFA_ERR_RING",
 }
 DECODE_MAX_L = 64
 EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_opt", "prefill_attn_gqa_varlen",

@@ -190,7 +190,7 @@ int prefill_attn_gqa_varlen_opt(const void* Q, const void* K, const void* V,
     return PFA_ERR_SIZE;
   if (max_seqlen_q > PFA_MAX_LEN || n_seq == INT_MAX) return PFA_ERR_SIZE;
   // packed row strides (Hq * D, Hkv * D elements) and a 64-key tile's byte extent stay in 31 bits
-  if (Hq > (1 << 24) / 128 || Hkv > (1 << 24) / 128) return PFA_ERR_SIZE;
+  if (Hq >= (1 << 24) / 128 || Hkv >= (1 << 24) / 128) return PFA_ERR_SIZE;
   const long long lim = LLONG_MAX / 4;
   long long q_elems, kv_elems, t;
   if (!mul_fits(total_q, Hq, lim, &t) || !mul_fits(t, D, lim, &q_elems)) return PFA_ERR_SIZE;
@@ -301,6 +301,9 @@ int prefill_attn_gqa_ring_opt(const void* Q, const void* K_new, const void* V_ne
   if (!Q || !K_new || !V_new || !K_ring || !V_ring || !O) return PFA_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1 || pos0 < 0 || ring < 1) return PFA_ERR_SIZE;
   if (static_cast<long long>(pos0) + L > PFA_MAX_LEN || ring > PFA_MAX_LEN) return PFA_ERR_SIZE;
+  // one (b, KV head) ring is addressed with 32-bit byte offsets (the tile descriptor's size and each
+  // row's slot offset), so it must stay under 2 GiB
+  if (static_cast<long long>(ring) * D * 2 >= (1LL << 31)) return PFA_ERR_SIZE;
   const long long lim = LLONG_MAX / 4;
   long long q_elems, new_elems, ring_elems, t;
   if (!mul_fits(B, Hq, lim, &t) || !mul_fits(t, L, lim, &t) || !mul_fits(t, D, lim, &q_elems)) return PFA_ERR_SIZE;

@@ -280,11 +280,11 @@ __global__ __launch_bounds__(64, (RB == 1 ? 2 : 1)) void pfa_decode_split_kernel
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      // key visible iff 0 <= key - lo <= span (one unsigned compare); an empty row gets lo past
-      // every key (key - lo < 0, a huge unsigned value) and span 0
+      // key visible iff 0 <= key - lo <= span (one unsigned compare); an empty row gets lo = -1
+      // and span 0, which only key -1 would pass: no key of any tile is visible to it
       const bool empty = row_hi[rb] < row_lo[rb];
       const unsigned span = empty ? 0u : (unsigned)(row_hi[rb] - row_lo[rb]);
-      const int lo = empty ? S + kTk : row_lo[rb];
+      const int lo = empty ? -1 : row_lo[rb];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -486,11 +486,13 @@ __global__ __launch_bounds__(64, 2) void pfa_decode_kreg_kernel(DParams p) {
     for (int v = 0; v < 16; ++v) acc[db][v] = 0.0f;
   float m = -INFINITY, l = 0.0f;
   const float c = SOFTCAP ? 1.0f : p.c;
-  // the row's keys within this split: [lo, min(hi, last key of tile t_end - 1)]
+  // the row's keys within this split: [lo, min(hi, last key of tile t_end - 1)]. A row with no
+  // key here gets lo_eff = -1 and span 0, which no key passes: the padding steps past t_end visit
+  // keys up to S + 95, so a sentinel past S could coincide with one of them.
   const int hi_split = min(hi, t_end * kTk - 1);
   const bool empty = hi_split < lo;
   const unsigned span = empty ? 0u : (unsigned)(hi_split - lo);
-  const int lo_eff = empty ? S + kTk : lo;
+  const int lo_eff = empty ? -1 : lo;
 
   // One step on tile t (K in kr, V in `cur`): wait for it (the next tile may stay in flight), the
   // scores, then tile t+2 to the buffers tile t-1 used (`nxt2`, kr2), softmax and P.V. The stages

@@ -15,3 +15,16 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(autouse=True, scope="session")
+def _blas_one_thread_per_worker():
+    """The oracle spreads its rows over a thread pool of one worker per host core; pin BLAS to one
+    thread per calling thread so the workers do not oversubscribe the cores."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        yield
+        return
+    with threadpool_limits(limits=1, user_api="blas"):
+        yield

@@ -83,9 +83,9 @@ def call(**kw):
     (dict(Hq=6, Hkv=4), 3), (dict(Hq=7, Hkv=2), 3),
     (dict(D=96), 4), (dict(D=256), 4), (dict(D=32), 4),
     (dict(off=-1, window=5), 5),
-    (dict(scale=float("nan")), 6), (dict(scale=float("inf")), 6), (dict(scale=0.0), 6), (dict(scale=-0.1), 6),
-    (dict(q=Q + 8), 7), (dict(k=K + 2), 7), (dict(v=V + 4), 7), (dict(o=O + 1), 7),
-    (dict(o=Q), 8), (dict(o=Q + 16), 8), (dict(o=K + 4096), 8), (dict(o=V - 16), 8), (dict(mask=O + 3), 8),
+    (dict(scale=float("nan")), 10), (dict(scale=float("inf")), 10), (dict(scale=0.0), 10), (dict(scale=-0.1), 10),
+    (dict(q=Q + 8), 6), (dict(k=K + 2), 6), (dict(v=V + 4), 6), (dict(o=O + 1), 6),
+    (dict(o=Q), 7), (dict(o=Q + 16), 7), (dict(o=K + 4096), 7), (dict(o=V - 16), 7), (dict(mask=O + 3), 7),
     (dict(flags=2), 9), (dict(flags=0x80000000), 9),
 ], ids=lambda x: str(x))
 def test_invalid_arguments_rejected(lib, kw, code):
@@ -99,9 +99,9 @@ def test_validation_order(lib):
     assert call(Hq=7, D=96) == 3
     assert call(D=96, off=-1, window=3) == 4
     assert call(off=-1, window=3, scale=0.0) == 5
-    assert call(scale=0.0, q=Q + 2) == 6
-    assert call(q=Q + 2, o=K) == 7
-    assert call(o=K, flags=4) == 8
+    assert call(scale=0.0, q=Q + 2) == 10
+    assert call(q=Q + 2, o=K) == 6
+    assert call(o=K, flags=4) == 7
 
 
 def test_o_adjacent_to_inputs_is_not_alias(lib):
@@ -151,24 +151,29 @@ def vcall(**kw):
     (dict(n=0), 2), (dict(maxq=0), 2), (dict(tq=0), 2), (dict(tk=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2),
     (dict(D=0), 2), (dict(maxq=2 ** 30 + 1), 2), (dict(n=2 ** 31 - 1), 2),
     (dict(Hq=2 ** 18, Hkv=2 ** 18), 2),
+    (dict(Hq=2 ** 17, Hkv=2 ** 17), 2),     # a 64-key tile of packed rows would span exactly 2^31 bytes
     (dict(maxq=2 ** 30, n=2 ** 20, Hq=64, Hkv=64), 2),
     (dict(Hq=6, Hkv=4), 3),
     (dict(D=96), 4),
     (dict(causal=0, window=8), 5),
-    (dict(scale=float("nan")), 6), (dict(scale=0.0), 6),
-    (dict(q=Q + 8), 7), (dict(o=O + 2), 7), (dict(cq=CQ + 2), 7), (dict(ck=CK + 1), 7),
-    (dict(o=Q), 8), (dict(o=K + 16), 8), (dict(o=V), 8), (dict(cq=O + 4), 8), (dict(ck=O + 100 * 4 * 128 * 2 - 4), 8),
+    (dict(scale=float("nan")), 10), (dict(scale=0.0), 10),
+    (dict(q=Q + 8), 6), (dict(o=O + 2), 6), (dict(cq=CQ + 2), 6), (dict(ck=CK + 1), 6),
+    (dict(o=Q), 7), (dict(o=K + 16), 7), (dict(o=V), 7), (dict(cq=O + 4), 7), (dict(ck=O + 100 * 4 * 128 * 2 - 4), 7),
 ], ids=lambda x: str(x))
 def test_varlen_invalid_arguments_rejected(lib, kw, code):
     assert vcall(**kw) == code
 
 
 def test_varlen_prefix_sums_adjacent_to_o_are_not_alias(lib):
-    # cu buffers may sit right after O ([O, O + total_q*Hq*D*2) is half-open); the first error after
-    # the alias check is the launch, which needs a GPU, so only the alias code is ruled out
+    # cu buffers may sit right after O ([O, O + total_q*Hq*D*2) is half-open). An unknown flag bit is
+    # checked after the alias rule, so PFA_ERR_FLAGS proves the alias check passed, and the call is
+    # stopped before anything could be launched at these fake addresses.
     o_bytes = 100 * 4 * 128 * 2
-    rc = vcall(cq=O + o_bytes, ck=O + o_bytes + 16)
-    assert rc != 8
+    a = dict(VGOOD, cq=O + o_bytes, ck=O + o_bytes + 16)
+    rc = pfa.prefill_attn_gqa_varlen_raw(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["n"], a["maxq"], a["tq"],
+                                         a["tk"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["window"],
+                                         a["o"], a["stream"], flags=2)
+    assert rc == 9
 
 
 def test_varlen_binding_rejects_bad_tensors():
@@ -198,10 +203,10 @@ def dcall(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), 1), (dict(o=0), 1), (dict(ws=0), 1),
     (dict(L=0), 2), (dict(S=0), 2), (dict(L=65), 2), (dict(B=2 ** 21), 2),
-    (dict(Hq=6, Hkv=4), 3), (dict(D=96), 4), (dict(off=-1, window=5), 5), (dict(scale=0.0), 6),
-    (dict(ws=WS + 8), 7), (dict(q=Q + 2), 7),
+    (dict(Hq=6, Hkv=4), 3), (dict(D=96), 4), (dict(off=-1, window=5), 5), (dict(scale=0.0), 10),
+    (dict(ws=WS + 8), 6), (dict(q=Q + 2), 6),
     (dict(wsb=0), 11), (dict(wsb=-1), 11),
-    (dict(ws=Q), 8), (dict(ws=O - 16), 8), (dict(ws=K + 64), 8),
+    (dict(ws=Q), 7), (dict(ws=O - 16), 7), (dict(ws=K + 64), 7),
 ], ids=lambda x: str(x))
 def test_decode_invalid_arguments_rejected(lib, kw, code):
     assert dcall(**kw) == code
@@ -242,26 +247,36 @@ def rcall(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), 1), (dict(kn=0), 1), (dict(vr=0), 1), (dict(o=0), 1),
     (dict(L=0), 2), (dict(pos0=-1), 2), (dict(ring=0), 2), (dict(pos0=2 ** 30), 2),
-    (dict(Hq=6, Hkv=4), 3), (dict(D=96), 4), (dict(scale=float("nan")), 6),
+    (dict(Hq=6, Hkv=4), 3), (dict(D=96), 4), (dict(scale=float("nan")), 10),
     (dict(ring=1038), 12),                      # < window - 1 + L = 1039
     (dict(ring=63, window=8, L=4), 12),         # < 64 slots
     (dict(window=0, ring=4096), 12),            # no window: needs pos0 + L = 5016 slots
-    (dict(kr=KR + 2), 7), (dict(o=O + 8), 7),
-    (dict(kr=Q), 8), (dict(vr=KN + 64), 8), (dict(o=KR), 8), (dict(kr=VR - 1024), 8),
+    (dict(kr=KR + 2), 6), (dict(o=O + 8), 6),
+    (dict(kr=Q), 7), (dict(vr=KN + 64), 7), (dict(o=KR), 7), (dict(kr=VR - 1024), 7),
 ], ids=lambda x: str(x))
 def test_ring_invalid_arguments_rejected(lib, kw, code):
     assert rcall(**kw) == code
 
 
+@pytest.mark.parametrize("D,ring,code", [
+    (128, 2 ** 23, 2), (128, 2 ** 23 + 64, 2), (64, 2 ** 24, 2),   # one (b, KV head) ring >= 2 GiB
+    (128, 2 ** 23 - 64, 7), (64, 2 ** 24 - 64, 7),                 # just under: the planted alias is next
+])
+def test_ring_byte_offsets_stay_in_31_bits(lib, D, ring, code):
+    # ring slots are addressed with 32-bit byte offsets; a ring of 2^31 bytes or more is refused
+    assert rcall(D=D, ring=ring, pos0=100, L=16, window=0, kr=4 * A, vr=7 * A, q=8 * A, kn=9 * A, vn=10 * A,
+                 o=8 * A) == code
+
+
 def test_ring_capacity_rule_counts_only_existing_keys(lib):
     # pos0 + L <= ring: every key fits even though window - 1 + L would not; the next error after the
     # capacity check is an alias planted on purpose
-    assert rcall(pos0=100, L=16, window=4096, ring=128, o=Q) == 8
+    assert rcall(pos0=100, L=16, window=4096, ring=128, o=Q) == 7
     assert rcall(pos0=200, L=16, window=4096, ring=128, o=Q) == 12
 
 
 # ---- options (soft-capping) ----
-@pytest.mark.parametrize("softcap,code", [(float("nan"), 6), (float("inf"), 6), (-1.0, 6)])
+@pytest.mark.parametrize("softcap,code", [(float("nan"), 10), (float("inf"), 10), (-1.0, 10)])
 def test_softcap_rejected(lib, softcap, code):
     a = dict(GOOD)
     assert pfa.prefill_attn_gqa_raw(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["L"], a["S"], a["D"],
@@ -323,8 +338,8 @@ def bcall(bias=BIAS, strides=(0, 0, 48), **kw):
     (dict(mask=M), 5),                                   # not with a key mask
     (dict(strides=(0, 0, -4)), 2), (dict(strides=(-4, 0, 48)), 2),
     (dict(strides=(0, 0, 2 ** 28)), 2),                 # one (b, h) block too large
-    (dict(bias=BIAS + 4), 7), (dict(strides=(0, 0, 50)), 7), (dict(strides=(2, 0, 48)), 7),
-    (dict(bias=O), 8), (dict(bias=O - 64), 8),
+    (dict(bias=BIAS + 4), 6), (dict(strides=(0, 0, 50)), 6), (dict(strides=(2, 0, 48)), 6),
+    (dict(bias=O), 7), (dict(bias=O - 64), 7),
 ], ids=lambda x: str(x))
 def test_bias_rejected(lib, kw, code):
     assert bcall(**kw) == code
@@ -355,14 +370,14 @@ def ocall(sinks=None, sel=None, blocks=(64, 64), sel_strides=(0, 0, 1), **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(sinks=SINKS + 2), 7),                          # sink logits: 4-byte aligned
-    (dict(sinks=O + 8), 8), (dict(sinks=O - 8), 8),     # and not overlapping O
+    (dict(sinks=SINKS + 2), 6),                          # sink logits: 4-byte aligned
+    (dict(sinks=O + 8), 7), (dict(sinks=O - 8), 7),     # and not overlapping O
     (dict(sel=SEL, blocks=(16, 64)), 2), (dict(sel=SEL, blocks=(48, 64)), 2),   # block_q % 32
     (dict(sel=SEL, blocks=(32, 32)), 2), (dict(sel=SEL, blocks=(32, 96)), 2),   # block_k % 64
     (dict(sel=SEL, blocks=(0, 64)), 2), (dict(sel=SEL, sel_strides=(0, -1, 1)), 2),
     (dict(sel=SEL, sel_strides=(1 << 62, 0, 1), B=2), 2),
     (dict(sel=SEL, mask=M), 5), (dict(sel=SEL, bias=BIAS), 5),  # not with a key mask or a bias
-    (dict(sel=O), 8), (dict(sel=O - 1, blocks=(32, 64)), 8),  # rows 0-31 and 32: 2 bytes from O - 1
+    (dict(sel=O), 7), (dict(sel=O - 1, blocks=(32, 64)), 7),  # rows 0-31 and 32: 2 bytes from O - 1
 ], ids=lambda x: str(x))
 def test_sinks_and_block_bitmap_rejected(lib, kw, code):
     assert ocall(**kw) == code
@@ -378,7 +393,7 @@ def test_block_bitmap_not_on_decode(lib):
     assert rc == 5
     assert pfa.prefill_attn_gqa_decode_raw(d["q"], d["k"], d["v"], d["B"], d["Hq"], d["Hkv"], d["L"], d["S"],
                                            d["D"], d["scale"], d["off"], d["window"], None, d["o"], d["ws"],
-                                           need, None, 0.0, 0, O + 2) == 7
+                                           need, None, 0.0, 0, O + 2) == 6
 
 
 def vocall(flags=0, softcap=0.0, sinks=None, bias=None, sel=None):
@@ -390,9 +405,9 @@ def vocall(flags=0, softcap=0.0, sinks=None, bias=None, sel=None):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(flags=2), 9), (dict(softcap=-1.0), 6), (dict(softcap=float("inf")), 6),
+    (dict(flags=2), 9), (dict(softcap=-1.0), 10), (dict(softcap=float("inf")), 10),
     (dict(bias=BIAS), 5), (dict(sel=SEL), 5),            # per dense row: not on the packed layout
-    (dict(sinks=SINKS + 2), 7), (dict(sinks=O + 4), 8),
+    (dict(sinks=SINKS + 2), 6), (dict(sinks=O + 4), 7),
 ], ids=lambda x: str(x))
 def test_varlen_options_rejected(lib, kw, code):
     assert vocall(**kw) == code
@@ -407,9 +422,9 @@ def rocall(flags=0, softcap=0.0, sinks=None, bias=None, sel=None):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(flags=2), 9), (dict(softcap=-1.0), 6), (dict(bias=BIAS), 5), (dict(sel=SEL), 5),
-    (dict(sinks=SINKS + 2), 7), (dict(sinks=O + 4), 8),
-    (dict(sinks=KR + 64), 8), (dict(sinks=VR), 8),        # the rings are written before the sinks are read
+    (dict(flags=2), 9), (dict(softcap=-1.0), 10), (dict(bias=BIAS), 5), (dict(sel=SEL), 5),
+    (dict(sinks=SINKS + 2), 6), (dict(sinks=O + 4), 7),
+    (dict(sinks=KR + 64), 7), (dict(sinks=VR), 7),        # the rings are written before the sinks are read
 ], ids=lambda x: str(x))
 def test_ring_options_rejected(lib, kw, code):
     assert rocall(**kw) == code

@@ -65,7 +65,29 @@ CASES = [
     # one visible key per row (window 1): the output is that key's value row, bit for bit
     ("l4_window1", 2, 8, 2, 128, 4, 300, 296, 1, None),
     ("l40_window1_rows160", 1, 16, 4, 64, 40, 1000, 960, 1, None),
+    # rows whose window starts after their split's last key while a padding step of the
+    # register-K kernel covers key S + 32 (a sentinel past S once made that key visible)
+    ("l8_window1_s388_padding", 1, 8, 8, 128, 8, 388, 380, 1, None),
+    ("l8_window3_s420", 1, 8, 8, 128, 8, 420, 412, 3, None),
 ]
+
+
+def small_window_cases(n=24, seed=77):
+    """Seeded random decode shapes with short windows (ragged key counts, 1 <= window < 64)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4]))
+        D = int(rng.choice([64, 128]))
+        L = int(rng.integers(1, 9))
+        S = int(rng.integers(L, 1500))
+        W = int(rng.integers(1, 64))
+        out.append((f"win{i}", 1, Hkv * G, Hkv, D, L, S, S - L, W, None))
+    return out
+
+
+CASES += small_window_cases()
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])

@@ -11,7 +11,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import prefill_attention_amd as pfa  # noqa: E402
-from oracle import NO_CAUSAL, bf16_bits_to_f64, oracle_sdpa, oracle_selected_rows  # noqa: E402
+from oracle import NO_CAUSAL, bf16_bits_to_f64, host_workers, oracle_sdpa  # noqa: E402
 from workloads import CONFIGS, make_inputs, random_bits  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 ATOL = RTOL = 2e-2
 RMS_RATIO = 1e-2
 DEV = "cuda:0"
-WORKERS = 16
+WORKERS = max(1, min(16, host_workers()))
 
 
 def dev_bf16(bits):
@@ -80,8 +80,10 @@ def small_case(B, Hq, Hkv, L, S, D, off, W=0, seed=0, mask=None, amp=1.0):
 # ----------------------------------------------------------------------------------------------
 # The workloads at full size
 # ----------------------------------------------------------------------------------------------
-FULL_ORACLE = ["causal_witness_33x47", "small_prompt_128", "sliding_w1024_d128", "sliding_w1024_d64"]
-SAMPLED = ["mid_ctx_8k", "long_ctx_32k", "bidir_padded_b8"]
+# every output element of every workload is compared with the oracle (the 8K / 32K chunks and the
+# batched padded workload take a few seconds of oracle time on the host's cores)
+FULL_ORACLE = ["causal_witness_33x47", "small_prompt_128", "sliding_w1024_d128", "sliding_w1024_d64",
+               "mid_ctx_8k", "long_ctx_32k", "bidir_padded_b8"]
 _cache = {}
 
 
@@ -99,32 +101,7 @@ def test_workload_full_oracle(name):
     print(check_close(to64(out), oracle_of(x), name), flush=True)
 
 
-def sample_picks(x, rng, n_random=24):
-    B, Hq, L = x["q"].shape[0], x["q"].shape[1], x["q"].shape[2]
-    G = Hq // x["k"].shape[1]
-    heads = sorted({0, G - 1, G, Hq - 1, Hq // 2})
-    rows = sorted({0, 1, 31, 32, 63, 64, 127, 128, 255, 256, L // 2, L - 129, L - 128, L - 2, L - 1} & set(range(L)))
-    picks = [(int(rng.integers(B)), h, r) for h in heads for r in rows]
-    picks += [(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(L))) for _ in range(n_random)]
-    if B > 1:
-        picks += [(b, 0, L - 1) for b in range(B)]
-    return picks
-
-
-@pytest.mark.parametrize("name", SAMPLED)
-def test_workload_sampled_rows(name):
-    x = inputs(name)
-    print(f"[parity] {name} {CONFIGS[name]} (sampled rows)", flush=True)
-    out = run(x)
-    picks = sample_picks(x, np.random.default_rng(1))
-    got = np.stack([to64(out[b, h, i]) for b, h, i in picks])
-    ref = oracle_selected_rows(x["q"], x["k"], x["v"], x["scale"], x["causal_offset"], x["window"],
-                               x["key_mask"], picks)
-    print(check_close(got, ref, name), flush=True)
-    assert torch.isfinite(out.float()).all()
-
-
-@pytest.mark.parametrize("name", FULL_ORACLE + SAMPLED)
+@pytest.mark.parametrize("name", FULL_ORACLE)
 def test_skip_is_bit_identical_to_no_skip(name):
     x = inputs(name)
     print(f"[bitwise] {name}", flush=True)

@@ -348,7 +348,39 @@ def pin_block_bitmap():
     ref = brute_sdpa(q[:, :, :7], kk, vv, 0.4, causal_offset=4, window=5, block_sel=sel, block_q=4, block_k=3)
     assert np.allclose(got, ref, atol=1e-12, rtol=0)
 
-PINS = [pin_sinks, pin_block_bitmap, pin_softcap, pin_additive_bias, pin_two_key_sigmoid, pin_rows_sum_to_one, pin_uniform_v_returns_v, pin_window_reductions,
+def pin_selected_rows_match_full_oracle():
+    """oracle_selected_rows (one row at a time, used at full workload sizes) equals the matching
+    rows of oracle_sdpa on small cases with every option: per-batch key masks, causal offset and
+    window, soft-cap, an additive bias broadcast as [L, S], [B, 1, L, S] and [1, Hq, 1, S], sinks
+    and a per-(b, h) block bitmap with B > 1. Every (b, h, i) triple is picked."""
+    rng = np.random.default_rng(2024)
+    B, Hq, Hkv, L, S, D = 2, 4, 2, 9, 13, 8
+    q, k, v = rng.standard_normal((B, Hq, L, D)), rng.standard_normal((B, Hkv, S, D)), rng.standard_normal((B, Hkv, S, D))
+    km = (rng.random((B, S)) < 0.7).astype(np.uint8)
+    km[:, 0] = 1
+    picks = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(L)]
+    sinks = rng.standard_normal(Hq)
+    cases = [
+        dict(causal_offset=4, window=5, key_mask=km, softcap=3.0),
+        dict(causal_offset=4, window=0, key_mask=None, bias=rng.standard_normal((L, S))),
+        dict(causal_offset=-1, window=0, key_mask=km, bias=rng.standard_normal((B, 1, L, S))),
+        dict(causal_offset=6, window=0, key_mask=None, bias=rng.standard_normal((1, Hq, 1, S)), sinks=sinks),
+        dict(causal_offset=4, window=7, key_mask=None, softcap=2.0, sinks=sinks,
+             block_sel=(rng.random((B, Hq, 3, 4)) < 0.6).astype(np.uint8), block_q=3, block_k=4),
+        dict(causal_offset=-1, window=0, key_mask=None,
+             block_sel=(rng.random((B, 1, 3, 4)) < 0.5).astype(np.uint8), block_q=3, block_k=4),
+    ]
+    for c in cases:
+        full = oracle_sdpa(q, k, v, 0.4, **c)
+        opts = {kk: vv for kk, vv in c.items() if kk not in ("causal_offset", "window", "key_mask")}
+        rows = oracle.oracle_selected_rows(q, k, v, 0.4, c["causal_offset"], c["window"], c["key_mask"], picks,
+                                           **opts)
+        want = np.array([full[b, h, i] for (b, h, i) in picks])
+        assert np.allclose(rows, want, atol=1e-12, rtol=0), sorted(c)
+        assert np.count_nonzero(np.abs(want).sum(axis=1)) > len(picks) // 2  # not vacuous
+
+
+PINS = [pin_selected_rows_match_full_oracle, pin_sinks, pin_block_bitmap, pin_softcap, pin_additive_bias, pin_two_key_sigmoid, pin_rows_sum_to_one, pin_uniform_v_returns_v, pin_window_reductions,
         pin_gqa_is_expanded_mha, pin_triu_counts, pin_zero_scale_prefix_means, pin_chunk_equals_tail,
         pin_key_padding, pin_brute_force]
 
@@ -580,6 +612,22 @@ def _bad_empty_rows(scores, v, sink=None):
 _attention_rows_orig = osdpa.attention_rows
 
 
+def _bad_bias_first_row(bias, shape, b, h, i):
+    # the bias row of query row 0 for every row
+    return np.broadcast_to(np.asarray(bias, dtype=np.float64), shape)[b, h, 0:1]
+
+
+def _bad_sel_batch0(block_sel, shape, block_q, block_k, b, h, i):
+    # the bitmap of batch element 0 for every batch element
+    B, Hq, L, S = shape
+    full = np.broadcast_to(np.asarray(block_sel), (B, Hq, -(-L // block_q), -(-S // block_k)))
+    return osdpa.block_selected(np.array([i]), S, full[0, h], block_q, block_k)
+
+
+def _bad_key_valid_batch0(key_mask, b):
+    return None if key_mask is None else (np.asarray(key_mask)[0] != 0)
+
+
 @pytest.mark.parametrize("attr,bad", [("kv_head_of", _bad_head_map), ("visible", _bad_causal),
                                       ("visible", _bad_window), ("visible", _bad_key_mask),
                                       ("attention_rows", _bad_scale),
@@ -593,11 +641,15 @@ _attention_rows_orig = osdpa.attention_rows
                                       ("attention_rows", _bad_sink_sign),
                                       ("attention_rows", _bad_sel_ignored),
                                       ("block_selected", _bad_sel_swapped_blocks),
-                                      ("block_selected", _bad_sel_transposed)],
+                                      ("block_selected", _bad_sel_transposed),
+                                      ("bias_of_row", _bad_bias_first_row),
+                                      ("sel_of_row", _bad_sel_batch0),
+                                      ("key_valid_of", _bad_key_valid_batch0)],
                          ids=["head_map_mod", "causal_plus_one", "window_plus_one", "key_mask_dropped",
                               "scale_dropped", "empty_rows_nan", "softcap_after_mask", "softcap_unscaled",
                               "bias_ignored", "bias_sign", "sink_ignored", "sink_scaled", "sink_sign",
-                              "sel_ignored", "sel_swapped_blocks", "sel_transposed"])
+                              "sel_ignored", "sel_swapped_blocks", "sel_transposed",
+                              "rows_bias_first_row", "rows_sel_batch0", "rows_key_mask_batch0"])
 def test_planted_mistake_is_caught(monkeypatch, attr, bad):
     monkeypatch.setattr(osdpa, attr, bad)
     caught = 0

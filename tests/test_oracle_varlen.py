@@ -105,8 +105,32 @@ def pin_options_match_dense():
         assert np.allclose(np.transpose(got[a0:a1], (1, 0, 2)), ref[0], atol=1e-12, rtol=0)
 
 
+def pin_selected_rows_match_full_oracle():
+    """oracle_varlen_rows (one row at a time, used at full workload sizes) equals the matching rows
+    of oracle_varlen for every (packed row, head) pair, on batches with sequences without rows,
+    sequences without keys, more rows than keys, a last sequence, windows, soft-cap and sinks."""
+    rng = np.random.default_rng(99)
+    Hq, Hkv, D = 4, 2, 8
+    for lq, lk, causal, window, softcap, sinks in [
+            ([5, 0, 4, 3], [7, 3, 4, 0], True, 0, 0.0, None),
+            ([3, 6, 0, 2], [3, 2, 5, 9], True, 3, 2.5, rng.standard_normal(Hq)),
+            ([0, 4, 4, 1], [2, 4, 0, 6], False, 0, 0.0, rng.standard_normal(Hq))]:
+        cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+        cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+        q = rng.standard_normal((int(cu_q[-1]), Hq, D))
+        k = rng.standard_normal((int(cu_k[-1]), Hkv, D))
+        v = rng.standard_normal((int(cu_k[-1]), Hkv, D))
+        full = oracle_varlen(q, k, v, cu_q, cu_k, 0.6, causal, window, softcap, sinks)
+        picks = [(r, h) for r in range(int(cu_q[-1])) for h in range(Hq)]
+        rows = ovl.oracle_varlen_rows(q, k, v, cu_q, cu_k, 0.6, causal, window, picks, softcap, sinks)
+        want = np.array([full[r, h] for (r, h) in picks])
+        assert np.allclose(rows, want, atol=1e-12, rtol=0), (lq, lk)
+        assert np.count_nonzero(np.abs(want).sum(axis=1)) > len(picks) // 3  # not vacuous
+
+
 PINS = [pin_single_sequence_is_dense, pin_equal_length_pair_count, pin_more_rows_than_keys,
-        pin_brute_force_ragged, pin_sequences_independent, pin_options_match_dense]
+        pin_brute_force_ragged, pin_sequences_independent, pin_options_match_dense,
+        pin_selected_rows_match_full_oracle]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -157,11 +181,26 @@ def _bad_head_map(h, Hq, Hkv):
     return h % Hkv
 
 
+def _bad_sequence_left(cu_q, r):
+    # the leftmost prefix sum <= r: a row right after a sequence without rows goes to that sequence
+    return int(np.searchsorted(np.asarray(cu_q, dtype=np.int64), r, side="left") - 1) if r > 0 else 0
+
+
+def _bad_sequence_off_by_one(cu_q, r):
+    return max(0, _seq_orig(cu_q, r) - 1)
+
+
+_seq_orig = ovl.sequence_of_row
+
+
 @pytest.mark.parametrize("mod,attr,bad", [(ovl, "varlen_visible", _bad_upper_left),
                                           (ovl, "varlen_visible", _bad_causal_plus_one),
                                           (ovl, "varlen_visible", _bad_window),
-                                          (ovl, "kv_head_of", _bad_head_map)],
-                         ids=["upper_left", "causal_plus_one", "window_plus_one", "head_map_mod"])
+                                          (ovl, "kv_head_of", _bad_head_map),
+                                          (ovl, "sequence_of_row", _bad_sequence_left),
+                                          (ovl, "sequence_of_row", _bad_sequence_off_by_one)],
+                         ids=["upper_left", "causal_plus_one", "window_plus_one", "head_map_mod",
+                              "rows_sequence_side_left", "rows_sequence_off_by_one"])
 def test_varlen_planted_mistake_is_caught(monkeypatch, mod, attr, bad):
     monkeypatch.setattr(mod, attr, bad)
     caught = 0
