@@ -297,6 +297,32 @@ int prefill_attn_gqa_decode_opt(const void* Q, const void* K, const void* V,
  * arguments), or -1 if the shape is invalid for it. */
 int64_t pfa_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D);
 
+/* Size of the library's own decode scratch array (64 MiB), the most that
+ * prefill_attn_gqa_decode_noalloc can use. */
+#define PFA_DECODE_SCRATCH_BYTES 67108864
+
+/*
+ * prefill_attn_gqa_decode_noalloc -- prefill_attn_gqa_decode_opt for callers that cannot allocate
+ * device memory or hand in a workspace (code under HIP graph capture, tight serving loops, runtimes
+ * that forbid allocation): the same arguments without the workspace, the same kernels and the same
+ * result bit for bit, with the partials kept in a device array that the library owns instead.
+ *
+ * The array holds PFA_DECODE_SCRATCH_BYTES; a shape whose pfa_decode_workspace_bytes() exceeds it is
+ * rejected with PFA_ERR_WORKSPACE (use prefill_attn_gqa_decode with a workspace then). Each GPU the
+ * library runs on holds one copy of the array from the module's load until the process ends; the
+ * call itself allocates nothing (no hipMalloc, no allocating library routine). Every call on a GPU
+ * shares that GPU's copy, so calls that overlap in time on one GPU (different streams or host
+ * threads without ordering) race on it and give undefined results; calls ordered on one stream are
+ * safe. No state is carried from one call to the next (every partial is rewritten before it is
+ * read). Returns a pfa_status code; PFA_ERR_LAUNCH also if the array's device address cannot be
+ * obtained on the current device.
+ */
+int prefill_attn_gqa_decode_noalloc(const void* Q, const void* K, const void* V,
+                                    int B, int Hq, int Hkv, int L, int S, int D,
+                                    float scale, int causal_offset, int window,
+                                    const uint8_t* key_mask, void* O, void* stream,
+                                    const pfa_options* opts);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* pfa_status_str(int status);
 

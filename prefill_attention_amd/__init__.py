@@ -4,6 +4,7 @@ The computation runs in ``libpfa.so`` (hand-written HIP); this package is its th
 """
 from ._binding import (  # noqa: F401
     DECODE_MAX_L,
+    DECODE_SCRATCH_BYTES,
     EXPORTS,
     FLAG_NO_SKIP,
     LIB_PATH,
@@ -16,6 +17,8 @@ from ._binding import (  # noqa: F401
     library,
     prefill_attn_gqa,
     prefill_attn_gqa_decode,
+    prefill_attn_gqa_decode_noalloc,
+    prefill_attn_gqa_decode_noalloc_raw,
     prefill_attn_gqa_decode_raw,
     prefill_attn_gqa_raw,
     prefill_attn_gqa_ring,

@@ -23,9 +23,11 @@ STATUS = {
     9: "PFA_ERR_FLAGS", 10: "PFA_ERR_SCALE", 11: "PFA_ERR_WORKSPACE", 12: "PFA_ERR_RING",
 }
 DECODE_MAX_L = 64
+DECODE_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_opt", "prefill_attn_gqa_varlen",
            "prefill_attn_gqa_varlen_opt", "prefill_attn_gqa_ring_opt",
            "prefill_attn_gqa_ring", "prefill_attn_gqa_decode", "prefill_attn_gqa_decode_opt",
+           "prefill_attn_gqa_decode_noalloc",
            "pfa_decode_workspace_bytes", "pfa_status_str", "pfa_version")
 
 
@@ -72,6 +74,8 @@ def library() -> ctypes.CDLL:
         lib.prefill_attn_gqa_decode.restype = ci
         lib.prefill_attn_gqa_decode_opt.argtypes = sig[:-1] + [vp, ctypes.c_int64, vp, ctypes.POINTER(Options)]
         lib.prefill_attn_gqa_decode_opt.restype = ci
+        lib.prefill_attn_gqa_decode_noalloc.argtypes = sig + [ctypes.POINTER(Options)]
+        lib.prefill_attn_gqa_decode_noalloc.restype = ci
         lib.pfa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
         lib.pfa_decode_workspace_bytes.restype = ctypes.c_int64
         lib.prefill_attn_gqa_ring.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp, vp]
@@ -329,9 +333,31 @@ def prefill_attn_gqa_decode_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: 
         key_mask_ptr or None, o_ptr, ws_ptr or None, ws_bytes, stream or None, ctypes.byref(opts)))
 
 
+def prefill_attn_gqa_decode_noalloc_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: int, Hkv: int, L: int,
+                                        S: int, D: int, scale: float, causal_offset: int, window: int,
+                                        key_mask_ptr: int | None, o_ptr: int, stream: int | None,
+                                        softcap: float = 0.0, flags: int = 0, sinks_ptr: int | None = None) -> int:
+    """Direct C-ABI call of the allocation-free decode entry point; returns the status code."""
+    opts = Options(flags, softcap, None, 0, 0, 0, sinks_ptr or None)
+    return int(library().prefill_attn_gqa_decode_noalloc(
+        q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
+        key_mask_ptr or None, o_ptr, stream or None, ctypes.byref(opts)))
+
+
+def prefill_attn_gqa_decode_noalloc(q, k, v, *, scale: float | None = None, causal: bool = True,
+                                    causal_offset: int | None = None, window: int = 0, key_mask=None, out=None,
+                                    softcap: float = 0.0, sinks=None, stream=None):
+    """prefill_attn_gqa_decode with the partials in the library's own device scratch array instead
+    of a workspace (nothing is allocated by the call; `out` must then be given by callers that cannot
+    allocate). Calls that overlap in time on one GPU race on that array."""
+    return prefill_attn_gqa_decode(q, k, v, scale=scale, causal=causal, causal_offset=causal_offset,
+                                   window=window, key_mask=key_mask, out=out, softcap=softcap, sinks=sinks,
+                                   stream=stream, _noalloc=True)
+
+
 def prefill_attn_gqa_decode(q, k, v, *, scale: float | None = None, causal: bool = True,
                             causal_offset: int | None = None, window: int = 0, key_mask=None, out=None,
-                            workspace=None, softcap: float = 0.0, sinks=None, stream=None):
+                            workspace=None, softcap: float = 0.0, sinks=None, stream=None, _noalloc=False):
     """Short-query (decode, L <= 64) grouped-query attention on torch tensors: the same arguments
     and result as prefill_attn_gqa, computed with the key range split over the chip and a
     deterministic merge. `workspace` is an optional uint8 GPU tensor of at least
@@ -374,12 +400,21 @@ def prefill_attn_gqa_decode(q, k, v, *, scale: float | None = None, causal: bool
     elif (out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or out.device != q.device
           or not out.is_contiguous()):
         raise ValueError("out must be a contiguous bf16 tensor shaped like q on q's device")
-    need = decode_workspace_bytes(B, Hq, Hkv, L, S, D)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     stream_ptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if _noalloc:
+        with torch.cuda.device(q.device):
+            rc = prefill_attn_gqa_decode_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
+                                                     float(scale), int(causal_offset), int(window), mask_ptr,
+                                                     out.data_ptr(), stream_ptr, float(softcap), 0,
+                                                     _sinks_ptr(sinks, Hq, q.device))
+        if rc != 0:
+            raise PfaError(rc, status_str(rc))
+        return out
+    need = decode_workspace_bytes(B, Hq, Hkv, L, S, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     with torch.cuda.device(q.device):
         rc = prefill_attn_gqa_decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
                                          float(scale), int(causal_offset), int(window), mask_ptr,

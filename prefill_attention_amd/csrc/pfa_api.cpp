@@ -385,10 +385,12 @@ int64_t pfa_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D) 
   return pfa::decode_plan(B, Hq, Hkv, L, S, D).workspace_bytes;
 }
 
-int prefill_attn_gqa_decode_opt(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L,
-                                int S, int D, float scale, int causal_offset, int window,
-                                const uint8_t* key_mask, void* O, void* workspace, int64_t workspace_bytes,
-                                void* stream, const pfa_options* opts) {
+// The decode call with a caller workspace (workspace != nullptr) or, for the allocation-free entry
+// point (workspace == nullptr), with the library's own device scratch array.
+static int decode_call(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L, int S, int D,
+                       float scale, int causal_offset, int window, const uint8_t* key_mask, void* O,
+                       void* workspace, int64_t workspace_bytes, bool library_scratch, void* stream,
+                       const pfa_options* opts) {
   const unsigned flags = opts ? opts->flags : 0u;
   const float softcap = opts ? opts->softcap : 0.0f;
   int rc = validate(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window, key_mask, O, flags);
@@ -397,14 +399,10 @@ int prefill_attn_gqa_decode_opt(const void* Q, const void* K, const void* V, int
   if (!std::isfinite(softcap) || softcap < 0.0f) return PFA_ERR_SCALE;
   // the decode path takes no additive bias and no block bitmap
   if (opts && (opts->bias || opts->block_sel)) return PFA_ERR_MASK_ARGS;
-  if (!workspace) return PFA_ERR_NULL;
+  if (!library_scratch && !workspace) return PFA_ERR_NULL;
   if (L > PFA_DECODE_MAX_L || B > (1 << 20) || Hq > (1 << 20)) return PFA_ERR_SIZE;
   const pfa::DecodePlan plan = pfa::decode_plan(B, Hq, Hkv, L, S, D);
   if (plan.n_partials > INT_MAX || static_cast<long long>(B) * Hq * L > INT_MAX) return PFA_ERR_SIZE;
-  if (reinterpret_cast<uintptr_t>(workspace) & 15u) return PFA_ERR_ALIGN;
-  if (workspace_bytes < plan.workspace_bytes) return PFA_ERR_WORKSPACE;
-  const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace);
-  const Range ws{w0, w0 + static_cast<uintptr_t>(plan.workspace_bytes)};
   const auto bytes = [](long long a, long long b, long long c, long long d) {
     return static_cast<uintptr_t>(a) * static_cast<uintptr_t>(b) * static_cast<uintptr_t>(c) *
            static_cast<uintptr_t>(d) * 2u;
@@ -412,13 +410,25 @@ int prefill_attn_gqa_decode_opt(const void* Q, const void* K, const void* V, int
   const auto at = [](const void* p, uintptr_t n) {
     return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + n};
   };
-  if (overlaps(ws, at(Q, bytes(B, Hq, L, D))) || overlaps(ws, at(K, bytes(B, Hkv, S, D))) ||
-      overlaps(ws, at(V, bytes(B, Hkv, S, D))) || overlaps(ws, at(O, bytes(B, Hq, L, D))) ||
-      (key_mask && overlaps(ws, at(key_mask, static_cast<uintptr_t>(B) * static_cast<uintptr_t>(S)))) ||
-      (opts && opts->sinks && overlaps(ws, at(opts->sinks, static_cast<uintptr_t>(Hq) * 4u))))
-    return PFA_ERR_ALIAS;
+  if (library_scratch) {
+    if (plan.workspace_bytes > PFA_DECODE_SCRATCH_BYTES) return PFA_ERR_WORKSPACE;
+  } else {
+    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return PFA_ERR_ALIGN;
+    if (workspace_bytes < plan.workspace_bytes) return PFA_ERR_WORKSPACE;
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace);
+    const Range ws{w0, w0 + static_cast<uintptr_t>(plan.workspace_bytes)};
+    if (overlaps(ws, at(Q, bytes(B, Hq, L, D))) || overlaps(ws, at(K, bytes(B, Hkv, S, D))) ||
+        overlaps(ws, at(V, bytes(B, Hkv, S, D))) || overlaps(ws, at(O, bytes(B, Hq, L, D))) ||
+        (key_mask && overlaps(ws, at(key_mask, static_cast<uintptr_t>(B) * static_cast<uintptr_t>(S)))) ||
+        (opts && opts->sinks && overlaps(ws, at(opts->sinks, static_cast<uintptr_t>(Hq) * 4u))))
+      return PFA_ERR_ALIAS;
+  }
   rc = check_sinks(opts, Hq, at(O, bytes(B, Hq, L, D)));
   if (rc != PFA_OK) return rc;
+  if (library_scratch) {
+    rc = pfa::decode_scratch(&workspace);  // the current device's copy of the library array
+    if (rc != PFA_OK) return rc;
+  }
   pfa::Launch p;
   p.q = Q;
   p.k = K;
@@ -441,6 +451,21 @@ int prefill_attn_gqa_decode_opt(const void* Q, const void* K, const void* V, int
   p.softcap = softcap;
   p.sinks = opts ? opts->sinks : nullptr;
   return pfa::launch_decode(p, plan, workspace);
+}
+
+int prefill_attn_gqa_decode_opt(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L,
+                                int S, int D, float scale, int causal_offset, int window,
+                                const uint8_t* key_mask, void* O, void* workspace, int64_t workspace_bytes,
+                                void* stream, const pfa_options* opts) {
+  return decode_call(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window, key_mask, O, workspace,
+                     workspace_bytes, false, stream, opts);
+}
+
+int prefill_attn_gqa_decode_noalloc(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L,
+                                    int S, int D, float scale, int causal_offset, int window,
+                                    const uint8_t* key_mask, void* O, void* stream, const pfa_options* opts) {
+  return decode_call(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window, key_mask, O, nullptr, 0, true,
+                     stream, opts);
 }
 
 int prefill_attn_gqa_decode(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L,

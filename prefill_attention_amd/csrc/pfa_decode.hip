@@ -20,6 +20,7 @@
 //    O^T = V^T . P^T with V^T read by ds_read_b64_tr_b16 and P from the score registers;
 //  * exact online softmax per tile in the base-2 domain (scores times scale * log2 e).
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <stdint.h>
 
 #include "../../include/pfa.h"
@@ -739,9 +740,33 @@ int launch_decode_variant(const pfa::Launch& L, const pfa::DecodePlan& plan, voi
   return PFA_OK;
 }
 
+// ---- the allocation-free variant's scratch: the partials live in a library-held device array ----
+// One copy per GPU (the module's device globals are instantiated on every device it is loaded on),
+// held until the process ends. Host code never passes `decode_scratch_array` itself to a kernel (on
+// the host it names a host-side stand-in): its device address is looked up per device with
+// hipGetSymbolAddress and kept in g_scratch_ptr.
+static __device__ __align__(256) char decode_scratch_array[PFA_DECODE_SCRATCH_BYTES];
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
 
 namespace pfa {
+
+int decode_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PFA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(decode_scratch_array)) != hipSuccess || a == nullptr)
+      return PFA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = a;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PFA_OK;
+}
 
 int launch_decode(const Launch& p, const DecodePlan& plan, void* workspace) {
   const bool two = plan.rows_cap > 32;

@@ -75,4 +75,8 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int L, int S, int D);
 // Enqueue the split kernel and the merge kernel. Returns PFA_OK or PFA_ERR_LAUNCH.
 int launch_decode(const Launch& p, const DecodePlan& plan, void* workspace);
 
+// Device address of the current device's copy of the library's decode scratch array
+// (PFA_DECODE_SCRATCH_BYTES), looked up once per device. Returns PFA_OK or PFA_ERR_LAUNCH.
+int decode_scratch(void** ptr);
+
 }  // namespace pfa

@@ -212,6 +212,31 @@ def test_decode_invalid_arguments_rejected(lib, kw, code):
     assert dcall(**kw) == code
 
 
+def nacall(**kw):
+    a = dict(DGOOD)
+    a.update(kw)
+    opts = pfa.Options(a.get("flags", 0), a.get("softcap", 0.0), a.get("bias"), 0, 0, 0, None, None, 0, 0, 0, 0, 0)
+    return pfa.library().prefill_attn_gqa_decode_noalloc(
+        a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["L"], a["S"], a["D"], ctypes.c_float(a["scale"]),
+        a["off"], a["window"], a["mask"], a["o"], None, ctypes.byref(opts))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(o=0), 1), (dict(L=0), 2), (dict(L=65), 2), (dict(Hq=6, Hkv=4), 3),
+    (dict(D=96), 4), (dict(scale=0.0), 10), (dict(q=Q + 2), 6), (dict(o=Q), 7), (dict(flags=1), 9),
+    (dict(bias=8 * A), 5),
+    # the shape needs more partials than the library's 64 MiB scratch array holds
+    (dict(B=64, Hq=64, Hkv=8, L=16, S=131072, off=131056), 11),
+], ids=lambda x: str(x))
+def test_decode_noalloc_invalid_arguments_rejected(lib, kw, code):
+    assert nacall(**kw) == code
+
+
+def test_decode_noalloc_scratch_limit_matches_workspace_rule(lib):
+    assert pfa.decode_workspace_bytes(64, 64, 8, 16, 131072, 128) > pfa.DECODE_SCRATCH_BYTES
+    assert pfa.decode_workspace_bytes(8, 32, 8, 64, 32768, 128) <= pfa.DECODE_SCRATCH_BYTES
+
+
 def test_decode_workspace_too_small_by_one_byte(lib):
     need = pfa.decode_workspace_bytes(1, 4, 2, 4, 1000, 128)
     assert need > 0 and need % 16 == 0
@@ -221,6 +246,7 @@ def test_decode_workspace_too_small_by_one_byte(lib):
 def test_decode_workspace_bytes_function(lib):
     defines, _ = header_defines()
     assert defines["PFA_DECODE_MAX_L"] == pfa.DECODE_MAX_L
+    assert defines["PFA_DECODE_SCRATCH_BYTES"] == pfa.DECODE_SCRATCH_BYTES
     assert pfa.decode_workspace_bytes(1, 32, 8, 1, 32768, 128) > 0
     for bad in [(0, 32, 8, 1, 100, 128), (1, 32, 8, 0, 100, 128), (1, 32, 8, 65, 100, 128), (1, 30, 8, 1, 100, 128),
                 (1, 32, 8, 1, 100, 96), (1, 32, 8, 1, 0, 128)]:
