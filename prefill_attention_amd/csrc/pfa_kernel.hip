@@ -348,7 +348,9 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   }
 
   // ---- per-wave row state ----
-  const int qw0 = q0 + wave * kWaveRows;
+  // the wave's first row, made scalar explicitly (the compiler cannot see that tid >> 6 is wave-
+  // uniform): every per-wave quantity derived from it, such as the tile views, then lives in SGPRs
+  const int qw0 = q0 + __builtin_amdgcn_readfirstlane(wave) * kWaveRows;
   const bool wave_active = qw0 < L;
   const int ii_last = wave_active ? ((L - 1 - qw0) < 31 ? (L - 1 - qw0) : 31) : 0;
 
@@ -440,8 +442,10 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   // bit is m_all's: whether every key of the returned tile is valid (no elementwise key masking
   // needed), or whether this wave's query block selects the tile.
   auto next_tile = [&](int k) __attribute__((always_inline)) -> int {
-    if (k >= kt_hi) return (kt_hi << 1) | 1;
+    // without a key mask or bitmap every tile of the range is visited; a k >= kt_hi (the end, or an
+    // empty range) is treated by every caller like kt_hi
     if (!kmask && !SEL) return (k << 1) | 1;
+    if (k >= kt_hi) return (kt_hi << 1) | 1;
     while (k < kt_hi) {
       ensure_chunk(k);
       if (p.no_skip) return (k << 1) | (int)((m_all >> (k & 63)) & 1ull);
@@ -554,8 +558,21 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     const long long t = (long long)causal_offset - W + 1 + qw0;
     return (int)(t < -512 ? -512 : (t > (long long)S + 512 ? (long long)S + 512 : t));
   }();
+  // Tiles that every row of the wave sees whole -- no causal, window or tail edge inside them, i.e.
+  // dc >= 63, dw <= -31 and lim_tail == 64 below -- are kt in [t_int_lo, t_int_hi]; with every key
+  // valid (or, with a block bitmap, the tile selected) their view is constant.
+  const int t_int_lo = (wbase + 31 + (kBN - 1)) >> 6;                 // ceil((wbase + 31) / 64)
+  const int t_int_hi = min((cbase - (kBN - 1)) >> 6, (S >> 6) - 1);  // floor((cbase - 63) / 64)
   auto view_of = [&](int kt, bool tile_bit) __attribute__((always_inline)) -> TileView {
     TileView tv;
+    if ((kt >= t_int_lo) & (kt <= t_int_hi) & tile_bit) {
+      tv.lim_tail = kBN;
+      tv.dc = 256;
+      tv.dw = -256;
+      tv.live = wave_active;
+      tv.need_mask = false;
+      return tv;
+    }
     const int key0 = kt * kBN;
     // a tile the wave's query block does not select is a tile without keys (lim_tail = 0)
     const bool selected = SEL ? tile_bit : true;
