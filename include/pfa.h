@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define PFA_VERSION 10700 /* 1.7.0 */
+#define PFA_VERSION 10800 /* 1.8.0 */
 
 /* causal_offset < 0 selects bidirectional attention (no causal term). */
 #define PFA_NO_CAUSAL (-1)
@@ -77,7 +77,7 @@ enum pfa_status {
   PFA_ERR_LAUNCH = 8,    /* the HIP launch failed (e.g. no gfx950 device is current)            */
   PFA_ERR_FLAGS = 9,     /* unknown bit in flags                                                */
   PFA_ERR_SCALE = 10,    /* scale not finite or not > 0; softcap not finite or < 0              */
-  PFA_ERR_WORKSPACE = 11, /* decode workspace smaller than pfa_decode_workspace_bytes()         */
+  PFA_ERR_WORKSPACE = 11, /* workspace smaller than pfa_{decode,prefill}_workspace_bytes()    */
   PFA_ERR_RING = 12       /* ring cache smaller than 64 slots or than the keys the chunk sees   */
 };
 
@@ -171,6 +171,42 @@ int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V,
                          float scale, int causal_offset, int window,
                          const uint8_t* key_mask, void* O, void* stream,
                          const pfa_options* opts);
+
+/*
+ * prefill_attn_gqa_ws -- prefill_attn_gqa_opt with a caller workspace that lets the call split the
+ * key range of a query block over several workgroups. prefill_attn_gqa runs one workgroup per query
+ * block (256 rows of one query head and batch element), so a call with fewer blocks than the
+ * chip's 256 compute units leaves units idle for its whole length (8 query heads, 2048 rows and 32K
+ * cached keys: 64 blocks). Here a fixed grid of 256 workgroups takes equal shares of the (query
+ * block, key tile) space; a block split between workgroups leaves one FP32 partial (running max,
+ * sum, accumulator) per part in the workspace, and the part that finishes last merges them in key
+ * order with the merge equations (tiny-llm Week 2 Day 5, Task 1) and writes O. The merge order is
+ * fixed, so results are run-to-run deterministic, and skipping is bit-identical to
+ * PFA_FLAG_NO_SKIP; they may differ in the last bits from prefill_attn_gqa (other summation
+ * boundaries). Both meet the same tolerance.
+ *
+ * When it pays: with B * Hq * ceil(L / 256) well below 256. With a few hundred blocks or more,
+ * prefill_attn_gqa is faster: its workgroups start together at the first key tile and walk the
+ * keys in step, so the K / V tiles of a KV head are fetched once per L2, while the shares of a
+ * split start at scattered key tiles.
+ *
+ * Same arguments as prefill_attn_gqa_opt, plus a DEVICE workspace of at least
+ * pfa_prefill_workspace_bytes(B, Hq, Hkv, L, S, D) bytes, 16-byte aligned, not overlapping any
+ * other buffer of the call, ZERO-FILLED before its first use (it holds one counter per query block,
+ * and every call leaves the counters zero again). Calls that share a workspace must be ordered on
+ * one stream. With an additive bias or a block bitmap the call runs as prefill_attn_gqa_opt and
+ * leaves the workspace untouched. Returns a pfa_status code (PFA_ERR_WORKSPACE if it is too small).
+ */
+int prefill_attn_gqa_ws(const void* Q, const void* K, const void* V,
+                        int B, int Hq, int Hkv, int L, int S, int D,
+                        float scale, int causal_offset, int window,
+                        const uint8_t* key_mask, void* O,
+                        void* workspace, int64_t workspace_bytes, void* stream,
+                        const pfa_options* opts);
+
+/* Workspace bytes prefill_attn_gqa_ws needs for this shape (a pure function of the arguments),
+ * or -1 if the shape is invalid for it. */
+int64_t pfa_prefill_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D);
 
 /*
  * prefill_attn_gqa_varlen -- the same attention over a packed batch of variable-length sequences

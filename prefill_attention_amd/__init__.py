@@ -21,6 +21,8 @@ from ._binding import (  # noqa: F401
     prefill_attn_gqa_decode_noalloc_raw,
     prefill_attn_gqa_decode_raw,
     prefill_attn_gqa_raw,
+    prefill_attn_gqa_ws_raw,
+    prefill_workspace_bytes,
     prefill_attn_gqa_ring,
     prefill_attn_gqa_ring_raw,
     prefill_attn_gqa_varlen,

@@ -27,7 +27,7 @@ DECODE_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("prefill_attn_gqa", "prefill_attn_gqa_ex", "prefill_attn_gqa_opt", "prefill_attn_gqa_varlen",
            "prefill_attn_gqa_varlen_opt", "prefill_attn_gqa_ring_opt",
            "prefill_attn_gqa_ring", "prefill_attn_gqa_decode", "prefill_attn_gqa_decode_opt",
-           "prefill_attn_gqa_decode_noalloc",
+           "prefill_attn_gqa_decode_noalloc", "prefill_attn_gqa_ws", "pfa_prefill_workspace_bytes",
            "pfa_decode_workspace_bytes", "pfa_status_str", "pfa_version")
 
 
@@ -76,6 +76,10 @@ def library() -> ctypes.CDLL:
         lib.prefill_attn_gqa_decode_opt.restype = ci
         lib.prefill_attn_gqa_decode_noalloc.argtypes = sig + [ctypes.POINTER(Options)]
         lib.prefill_attn_gqa_decode_noalloc.restype = ci
+        lib.prefill_attn_gqa_ws.argtypes = sig[:-1] + [vp, ctypes.c_int64, vp, ctypes.POINTER(Options)]
+        lib.prefill_attn_gqa_ws.restype = ci
+        lib.pfa_prefill_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
+        lib.pfa_prefill_workspace_bytes.restype = ctypes.c_int64
         lib.pfa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
         lib.pfa_decode_workspace_bytes.restype = ctypes.c_int64
         lib.prefill_attn_gqa_ring.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp, vp]
@@ -116,6 +120,23 @@ def prefill_attn_gqa_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: int, Hk
         key_mask_ptr or None, o_ptr, stream or None, ctypes.byref(opts)))
 
 
+def prefill_workspace_bytes(B: int, Hq: int, Hkv: int, L: int, S: int, D: int) -> int:
+    """Bytes of workspace prefill_attn_gqa_ws needs for this shape (-1 if invalid)."""
+    return int(library().pfa_prefill_workspace_bytes(B, Hq, Hkv, L, S, D))
+
+
+def prefill_attn_gqa_ws_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: int, Hkv: int, L: int,
+                            S: int, D: int, scale: float, causal_offset: int, window: int,
+                            key_mask_ptr: int | None, o_ptr: int, ws_ptr: int | None, ws_bytes: int,
+                            stream: int | None, flags: int = 0, softcap: float = 0.0,
+                            sinks_ptr: int | None = None) -> int:
+    """Direct C-ABI call of the key-split prefill entry point; returns the status code."""
+    opts = Options(flags, softcap, None, 0, 0, 0, sinks_ptr or None)
+    return int(library().prefill_attn_gqa_ws(
+        q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
+        key_mask_ptr or None, o_ptr, ws_ptr or None, ws_bytes, stream or None, ctypes.byref(opts)))
+
+
 def _sinks_ptr(sinks, Hq, device):
     """Device pointer of a float32 [Hq] sink-logit tensor (None passes through)."""
     if sinks is None:
@@ -131,7 +152,7 @@ def _sinks_ptr(sinks, Hq, device):
 def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True,
                      causal_offset: int | None = None, window: int = 0, key_mask=None, out=None,
                      no_skip: bool = False, softcap: float = 0.0, bias=None, sinks=None,
-                     block_sel=None, block_q: int = 0, block_k: int = 0, stream=None):
+                     block_sel=None, block_q: int = 0, block_k: int = 0, stream=None, workspace=None):
     """Grouped-query prefill attention on torch tensors.
 
     q: bf16 [B,Hq,L,D]; k, v: bf16 [B,Hkv,S,D]; key_mask: optional uint8/bool [B,S] (nonzero =
@@ -231,6 +252,22 @@ def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     stream_ptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if workspace is not None:
+        # the key-split entry point (prefill_attn_gqa_ws): a zero-filled uint8 GPU tensor of at least
+        # prefill_workspace_bytes(...) bytes, reused by calls ordered on one stream
+        if bias is not None or block_sel is not None:
+            raise ValueError("the workspace (key-split) call takes no bias or block bitmap")
+        if (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or workspace.device != q.device
+                or not workspace.is_contiguous()):
+            raise ValueError(f"workspace must be a contiguous uint8 tensor on {q.device}")
+        with torch.cuda.device(q.device):
+            rc = prefill_attn_gqa_ws_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
+                                         float(scale), int(causal_offset), int(window), mask_ptr, out.data_ptr(),
+                                         workspace.data_ptr(), workspace.numel(), stream_ptr,
+                                         FLAG_NO_SKIP if no_skip else 0, float(softcap), sinks_ptr)
+        if rc != 0:
+            raise PfaError(rc, status_str(rc))
+        return out
     with torch.cuda.device(q.device):
         rc = prefill_attn_gqa_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
                                   float(scale), int(causal_offset), int(window), mask_ptr,

@@ -80,9 +80,18 @@ int check_sinks(const pfa_options* opts, int Hq, Range out) {
 
 extern "C" {
 
-int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv,
-                         int L, int S, int D, float scale, int causal_offset, int window,
-                         const uint8_t* key_mask, void* O, void* stream, const pfa_options* opts) {
+// Workspace of the key-split prefill for this shape: the FP32 partial slots, then one counter per
+// item (query block of a query head and batch element), rounded to 16 bytes.
+static long long prefill_workspace_bytes(int B, int Hq, int L, int D) {
+  const long long items = static_cast<long long>(B) * Hq * ((static_cast<long long>(L) + pfa::rows_per_block(D) - 1) /
+                                                            pfa::rows_per_block(D));
+  return pfa::split_part_bytes(D) + (items * 4 + 15) / 16 * 16;
+}
+
+// prefill_attn_gqa_opt (workspace == nullptr, use_ws false) or prefill_attn_gqa_ws.
+static int prefill_call(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L, int S, int D,
+                        float scale, int causal_offset, int window, const uint8_t* key_mask, void* O, void* stream,
+                        const pfa_options* opts, bool use_ws, void* workspace, int64_t workspace_bytes) {
   const unsigned flags = opts ? opts->flags : 0u;
   const float softcap = opts ? opts->softcap : 0.0f;
   int rc = validate(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window, key_mask, O,
@@ -124,6 +133,22 @@ int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V, int B, int
     const Range rs{reinterpret_cast<uintptr_t>(sel), reinterpret_cast<uintptr_t>(sel) + static_cast<uintptr_t>(last)};
     if (overlaps(ro, rs)) return PFA_ERR_ALIAS;
   }
+  if (use_ws) {
+    if (!workspace) return PFA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return PFA_ERR_ALIGN;
+    const long long need = prefill_workspace_bytes(B, Hq, L, D);
+    if (workspace_bytes < need) return PFA_ERR_WORKSPACE;
+    const auto at = [](const void* ptr, uintptr_t n) {
+      return Range{reinterpret_cast<uintptr_t>(ptr), reinterpret_cast<uintptr_t>(ptr) + n};
+    };
+    const Range ws = at(workspace, static_cast<uintptr_t>(need));
+    const uintptr_t kv_bytes = static_cast<uintptr_t>(B) * Hkv * static_cast<uintptr_t>(S) * D * 2u;
+    if (overlaps(ws, at(Q, static_cast<uintptr_t>(q_elems_o) * 2u)) || overlaps(ws, at(K, kv_bytes)) ||
+        overlaps(ws, at(V, kv_bytes)) || overlaps(ws, ro) ||
+        (key_mask && overlaps(ws, at(key_mask, static_cast<uintptr_t>(B) * static_cast<uintptr_t>(S)))) ||
+        (opts && opts->sinks && overlaps(ws, at(opts->sinks, static_cast<uintptr_t>(Hq) * 4u))))
+      return PFA_ERR_ALIAS;
+  }
   pfa::Launch p;
   p.q = Q;
   p.k = K;
@@ -144,6 +169,7 @@ int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V, int B, int
   p.flags = flags;
   p.stream = stream;
   p.softcap = softcap;
+  p.workspace = use_ws ? workspace : nullptr;
   if (bias) {
     p.bias = bias;
     p.bias_sb = opts->bias_stride_b;
@@ -162,6 +188,27 @@ int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V, int B, int
   }
   if (pfa::grid_blocks(p) > INT_MAX) return PFA_ERR_SIZE;
   return pfa::launch_prefill(p);
+}
+
+int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv,
+                         int L, int S, int D, float scale, int causal_offset, int window,
+                         const uint8_t* key_mask, void* O, void* stream, const pfa_options* opts) {
+  return prefill_call(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window, key_mask, O, stream, opts, false,
+                      nullptr, 0);
+}
+
+int prefill_attn_gqa_ws(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int L, int S, int D,
+                        float scale, int causal_offset, int window, const uint8_t* key_mask, void* O,
+                        void* workspace, int64_t workspace_bytes, void* stream, const pfa_options* opts) {
+  return prefill_call(Q, K, V, B, Hq, Hkv, L, S, D, scale, causal_offset, window, key_mask, O, stream, opts, true,
+                      workspace, workspace_bytes);
+}
+
+int64_t pfa_prefill_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || S < 1 || Hq % Hkv != 0 || (D != 64 && D != 128) || L > PFA_MAX_LEN ||
+      S > PFA_MAX_LEN || B > (1 << 20) || Hq > (1 << 20))
+    return -1;
+  return prefill_workspace_bytes(B, Hq, L, D);
 }
 
 int prefill_attn_gqa_ex(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv,
@@ -489,7 +536,7 @@ const char* pfa_status_str(int status) {
     case PFA_ERR_ALIAS: return "O must not overlap Q, K, V or key_mask";
     case PFA_ERR_FLAGS: return "unknown flag bit";
     case PFA_ERR_LAUNCH: return "HIP kernel launch failed (is a gfx950 device current?)";
-    case PFA_ERR_WORKSPACE: return "workspace smaller than pfa_decode_workspace_bytes() for this shape";
+    case PFA_ERR_WORKSPACE: return "workspace smaller than pfa_decode_workspace_bytes() / pfa_prefill_workspace_bytes() for this shape (or, for the allocation-free decode call, than the library's scratch array)";
     case PFA_ERR_RING: return "ring cache must have >= 64 slots and hold every visible key (window - 1 + L, or pos0 + L without a window)";
     default: return "unknown status";
   }

@@ -43,7 +43,20 @@ struct Launch {
   const uint8_t* sel = nullptr;
   int sel_bq = 0, sel_bk = 0;
   long long sel_sb = 0, sel_sh = 0, sel_sq = 0;
+  // Key-split workspace (null = one workgroup per item): split_part_bytes(d) of FP32 partials, then
+  // one zero counter per item (zero on entry, left zero on return).
+  void* workspace = nullptr;
 };
+
+// Workgroups of a key-split launch (one per compute unit of an MI355X).
+constexpr int kSplitWorkgroups = 256;
+
+// Bytes of FP32 partial slots a key-split launch uses (two per workgroup), before the counters.
+long long split_part_bytes(int d);
+
+// Whether launch_prefill runs the key split for this call (a workspace is given and the layout is
+// the dense one without bias, block bitmap or rotating cache).
+bool split_applies(const Launch& p);
 
 // Query rows handled by one workgroup of the prefill kernel.
 int rows_per_block(int d);

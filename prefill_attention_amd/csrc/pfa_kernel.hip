@@ -126,6 +126,12 @@ struct Params {
   int sel_bq, sel_bk;
   long long sel_sb, sel_sh, sel_sq;
   int no_skip;
+  // Key-split (stream) launch: nullptr = one workgroup per item. Otherwise gridDim.x workgroups
+  // each take an equal share of the linear (item, key tile) space; a part of an item leaves its
+  // FP32 partial in ws_part and the last part to finish merges them (ws_cnt: per-item counters,
+  // zero between calls).
+  float* ws_part;
+  unsigned* ws_cnt;
   int batch;
   int n_qblk;
   int n_wg;
@@ -249,8 +255,62 @@ constexpr int kModeSoftcap = 4;
 constexpr int kModeBias = 8;
 constexpr int kModeSel = 16;
 
+// Key tiles [lo, hi) that query rows [q0, q1) can see (dense layout, skipping on): the causal edge
+// bounds hi, the window edge lo.
+struct TileRange {
+  int lo, hi;
+};
+__device__ __forceinline__ TileRange skip_range(int q0, int q1, int S, int causal, int causal_offset, int W) {
+  const int n_tiles = (S + kBN - 1) / kBN;
+  TileRange r{0, n_tiles};
+  if (causal) {
+    long long hi_key = (long long)q1 + causal_offset;  // exclusive
+    if (hi_key > S) hi_key = S;
+    if (hi_key < 0) hi_key = 0;
+    r.hi = (int)((hi_key + kBN - 1) / kBN);
+    if (W > 0) {
+      long long lo_key = (long long)q0 + causal_offset - W + 1;
+      if (lo_key < 0) lo_key = 0;
+      const long long t = lo_key / kBN;
+      r.lo = (int)(t < n_tiles ? t : n_tiles);
+    }
+  }
+  return r;
+}
+
+// One piece of work of a workgroup: an item (kv head, query block, batch element, head in group)
+// and the part [t_from, t_to) of its n key tiles (counted from the item's first tile with skipping
+// on). A piece that is not the whole item writes an FP32 partial to workspace slot `slot`; the
+// item's parts are the consecutive workgroups v_first .. v_first + n_parts - 1 of the key split.
+struct Piece {
+  int item;
+  int t_from, t_to, n;
+  bool whole;
+  bool first;  // the workgroup's first piece: the LDS stages still have to be zeroed
+  int slot;
+  int v_first, n_parts;
+};
+
+// Workspace slot of a part: two per workgroup v of the split, 2v for a part that continues an item
+// (it starts inside it), 2v + 1 for a part that starts an item and ends inside it.
+__device__ __forceinline__ int part_slot(int v, bool starts_item) { return 2 * v + (starts_item ? 1 : 0); }
+
+// Device-coherent (agent-scope) FP32 store and load of a key-split partial.
+__device__ __forceinline__ void store_coherent(float* a, float x) {
+  __hip_atomic_store(a, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* a) {
+  return __hip_atomic_load(const_cast<float*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D>
+struct Slot {
+  static constexpr int kRegs = 16 * (D / 32) + 2;   // accumulator registers, reference max, sum
+  static constexpr int kFloats = kWaves * 64 * kRegs;
+};
+
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
+__device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc) {
   constexpr bool KMASK = (MODE & kModeKeyMask) != 0;
   constexpr bool RING = (MODE & kModeRing) != 0;
   constexpr bool SOFTCAP = (MODE & kModeSoftcap) != 0;
@@ -282,8 +342,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   // the 8 XCDs round-robin and blockIdx is remapped accordingly) every XCD holds whole KV heads of
   // every batch element: the workgroups that share a K/V tile share an L2, and sequences of
   // different lengths spread over all XCDs. Rank 0 is each sequence's heaviest causal block.
-  int item = blockIdx.x;
-  if (p.xcd_remap) item = (blockIdx.x % kXcds) * (p.n_wg / kXcds) + blockIdx.x / kXcds;
+  int item = pc.item;
   const int g = item % p.group;
   item /= p.group;
   const int b = item % p.batch;
@@ -331,20 +390,18 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   const uint8_t* mrow = KMASK ? p.key_mask + (long long)b * S : nullptr;
   constexpr bool kmask = KMASK;
 
-  // ---- key-tile range of the workgroup ----
+  // ---- key-tile range of the piece ----
+  // Skipping on: the tiles the block's rows can see, or the piece's part of them. Under NO_SKIP
+  // the first part of an item starts at tile 0 and the last one ends at the last tile, so both
+  // runs split an item at the same tiles and the extra tiles (fully masked) leave every partial
+  // bit for bit as it was.
   const int n_tiles = (S + kBN - 1) / kBN;
-  int kt_lo = 0, kt_hi = n_tiles;
-  if (!p.no_skip && causal) {
-    long long hi_key = (long long)q1 + causal_offset;  // exclusive
-    if (hi_key > S) hi_key = S;
-    if (hi_key < 0) hi_key = 0;
-    kt_hi = (int)((hi_key + kBN - 1) / kBN);
-    if (W > 0) {
-      long long lo_key = (long long)q0 + causal_offset - W + 1;
-      if (lo_key < 0) lo_key = 0;
-      const long long t = lo_key / kBN;
-      kt_lo = (int)(t < n_tiles ? t : n_tiles);
-    }
+  const TileRange sr = skip_range(q0, q1, S, causal, causal_offset, W);
+  int kt_lo = pc.whole ? sr.lo : sr.lo + pc.t_from;
+  int kt_hi = pc.whole ? sr.hi : sr.lo + pc.t_to;
+  if (p.no_skip) {
+    if (pc.whole || pc.t_from == 0) kt_lo = 0;
+    if (pc.whole || pc.t_to == pc.n) kt_hi = n_tiles;
   }
 
   // ---- per-wave row state ----
@@ -825,8 +882,11 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
   // zeroed once, so that a stage read before any tile lands there holds finite data. The zeroing
   // is done by fetches from an empty buffer descriptor (they write zeros), issued behind the first
   // tile's fetch so that both are in flight together.
+  // (a later piece of the workgroup reuses the stages: every wave has left the previous piece's
+  // loop, whose last barrier follows its last LDS read, before any wave gets here; the stages
+  // then hold that piece's finite tiles)
   if (cur < kt_hi) issue(cur, 0);
-  {
+  if (pc.first) {
     constexpr int kPerWave = G::kStageBytes / 1024 / kWaves;  // 1 KB fetches per wave and stage
     unsigned zoff[kPerWave];
 #pragma unroll
@@ -921,6 +981,55 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     main_loop(group_a);
   }
 
+  // ---- a part of an item: its partial to the workspace; the last part to finish merges ----
+  if (!pc.whole) {
+    using SL = Slot<D>;
+    __shared__ int s_last;
+    float* mine = p.ws_part + (size_t)pc.slot * SL::kFloats + (size_t)wave * SL::kRegs * 64 + lane;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) store_coherent(mine + (16 * db + v) * 64, acc[db][v]);
+    store_coherent(mine + (16 * DB) * 64, mref);
+    store_coherent(mine + (16 * DB + 1) * 64, l_run);
+    // Partials are written and read with device-coherent accesses (through to the memory side,
+    // past the per-XCD L2s) instead of a device-wide fence: such a fence writes back and
+    // invalidates this XCD's whole L2, which the other workgroups there are streaming K / V
+    // through. Every store has completed before the count is raised, and the last part's loads
+    // are issued only after its count has returned.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&p.ws_cnt[pc.item], 1u) + 1u == (unsigned)pc.n_parts;
+    __syncthreads();
+    if (!s_last) return;
+    // merge the parts in their key order, whichever finished last: the merge equations (tiny-llm
+    // Task 1) on (reference max, sum, accumulator), in the base-2 domain
+    mref = -INFINITY;
+    l_run = 0.0f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[db][v] = 0.0f;
+    for (int k = 0; k < pc.n_parts; ++k) {
+      const int sl = part_slot(pc.v_first + k, k == 0);
+      const float* src = p.ws_part + (size_t)sl * SL::kFloats + (size_t)wave * SL::kRegs * 64 + lane;
+      const float mk = load_coherent(src + (16 * DB) * 64);
+      const float lk = load_coherent(src + (16 * DB + 1) * 64);
+      const float mn = max2(mref, mk);
+      // a part without visible keys (mk = -inf, lk = 0, zero accumulator) changes nothing; while
+      // both are -inf the factors stay 1 (no -inf - -inf)
+      const float a0 = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref - mn);
+      const float a1 = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mk - mn);
+      l_run = l_run * a0 + lk * a1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] = acc[db][v] * a0 + load_coherent(src + (16 * db + v) * 64) * a1;
+      mref = mn;
+    }
+    if (tid == 0) __hip_atomic_store(&p.ws_cnt[pc.item], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
+  }
+
   // ---- epilogue: O = acc / l, rows without visible keys -> 0 ----
   if (!wave_active) return;
   float lt = l_run + __shfl_xor(l_run, 32);
@@ -939,6 +1048,147 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(acc[db][4 * j + i] * inv);
       *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * j + 4 * hh) = ov;
+    }
+  }
+}
+
+// The key split's walk over its linear (item, key tile) space: items in the order of the per-item
+// grid (KV head slowest, then query-block rank, batch element, head in group), each with the tiles
+// of its query block; the tile count depends on the rank only. Workgroup v of Pe takes tiles
+// [T v / Pe, T (v + 1) / Pe). One thread keeps the walk in LDS and advances it between pieces, so
+// nothing of it is held in registers across a piece.
+struct SplitWalk {
+  long long T, T_head, per_block;  // tiles in all, tiles of one KV head, items per (KV head, rank)
+  long long base;                  // linear start of the current (KV head, rank) block
+  long long in_block;              // item within that block
+  long long pos, r1;               // next tile of the share, end of the share
+  int hk, qrank, n, nb, Pe, v;
+  int done;
+  Piece pc;
+};
+
+// Tiles of query-block rank qrank (skipping on). A block whose rows see no key (a window past the
+// last key) weighs one tile: it is then always a whole piece of some workgroup, which runs its
+// true (empty) range and writes zeros.
+__device__ __forceinline__ int split_tiles_of(const Params& p, int qrank, int nb) {
+  const int qblk = p.causal ? (nb - 1 - qrank) : qrank;
+  const int q0 = qblk * kBM;
+  const int q1 = (q0 + kBM) < p.lq ? (q0 + kBM) : p.lq;
+  const TileRange r = skip_range(q0, q1, p.sk, p.causal, p.causal_offset, p.window);
+  return r.hi - r.lo > 1 ? r.hi - r.lo : 1;
+}
+
+// Workgroup of the split whose share holds linear tile t.
+__device__ __forceinline__ int split_wg_of(const SplitWalk& w, long long t) {
+  auto start_of = [&](int k) -> long long { return w.T * k / w.Pe; };
+  int k = (int)(t * w.Pe / w.T);
+  while (k + 1 < w.Pe && start_of(k + 1) <= t) ++k;
+  while (k > 0 && start_of(k) > t) --k;
+  return k;
+}
+
+// The piece at w.pos (w.pos < w.r1), or done.
+__device__ __forceinline__ void split_piece(SplitWalk& w, bool first) {
+  if (w.pos >= w.r1) {
+    w.done = 1;
+    return;
+  }
+  const long long I = w.base + w.in_block * w.n;  // the item's first linear tile
+  Piece& pc = w.pc;
+  pc.item = (int)(((long long)w.hk * w.nb + w.qrank) * w.per_block + w.in_block);
+  pc.n = w.n;
+  pc.t_from = (int)(w.pos - I);
+  pc.t_to = (int)((w.r1 - I) < w.n ? (w.r1 - I) : w.n);
+  pc.whole = pc.t_from == 0 && pc.t_to == w.n;
+  pc.first = first;
+  pc.slot = part_slot(w.v, pc.t_from == 0);
+  pc.v_first = pc.whole ? w.v : split_wg_of(w, I);
+  pc.n_parts = pc.whole ? 1 : split_wg_of(w, I + w.n - 1) - pc.v_first + 1;
+  w.pos = I + pc.t_to;
+}
+
+__device__ __forceinline__ void split_init(const Params& p, SplitWalk& w) {
+  const int P = gridDim.x;  // a multiple of kXcds
+  // v follows the hardware's round-robin over the 8 XCDs, so each XCD takes a contiguous eighth of
+  // the space (whole KV heads, when the heads divide evenly)
+  w.v = (blockIdx.x % kXcds) * (P / kXcds) + blockIdx.x / kXcds;
+  w.nb = (p.lq + kBM - 1) / kBM;
+  w.per_block = (long long)p.batch * p.group;
+  w.T_head = 0;
+  for (int r = 0; r < w.nb; ++r) w.T_head += w.per_block * split_tiles_of(p, r, w.nb);
+  w.T = w.T_head * p.hkv;
+  // with fewer tiles than workgroups only the first T take a share, so every share is non-empty
+  // and the parts of an item are consecutive workgroups
+  w.Pe = (int)(w.T < P ? w.T : P);
+  w.done = 0;
+  if (w.v >= w.Pe) {
+    w.done = 1;
+    return;
+  }
+  const long long r0 = w.T * w.v / w.Pe;
+  w.r1 = w.T * (w.v + 1) / w.Pe;
+  // locate r0: KV head, rank, item within the (head, rank) block
+  w.hk = (int)(r0 / w.T_head);
+  long long rem = r0 - w.hk * w.T_head;
+  w.base = w.hk * w.T_head;
+  w.qrank = 0;
+  w.n = split_tiles_of(p, 0, w.nb);
+  while (rem >= w.per_block * w.n) {
+    rem -= w.per_block * w.n;
+    w.base += w.per_block * w.n;
+    ++w.qrank;
+    w.n = split_tiles_of(p, w.qrank, w.nb);
+  }
+  w.in_block = rem / w.n;
+  w.pos = r0;
+  split_piece(w, true);
+}
+
+__device__ __forceinline__ void split_next(const Params& p, SplitWalk& w) {
+  if (++w.in_block == w.per_block) {
+    w.in_block = 0;
+    w.base += w.per_block * w.n;
+    if (++w.qrank == w.nb) {
+      w.qrank = 0;
+      ++w.hk;
+    }
+    w.n = split_tiles_of(p, w.qrank, w.nb);
+  }
+  split_piece(w, false);
+}
+
+template <int D, int MODE, bool SPLIT>
+__global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
+  if constexpr (!SPLIT) {
+    // one workgroup per item
+    int item = blockIdx.x;
+    if (p.xcd_remap) item = (blockIdx.x % kXcds) * (p.n_wg / kXcds) + blockIdx.x / kXcds;
+    Piece pc{};
+    pc.item = item;
+    pc.whole = true;
+    pc.first = true;
+    prefill_piece<D, MODE>(p, pc);
+  } else {
+    // key split (dense layout): a fixed grid, each workgroup its share of the linear space
+    __shared__ SplitWalk walk;
+    if (threadIdx.x == 0) split_init(p, walk);
+    __syncthreads();
+    for (;;) {
+      if (__builtin_amdgcn_readfirstlane(walk.done)) break;
+      Piece pc;
+      pc.item = __builtin_amdgcn_readfirstlane(walk.pc.item);
+      pc.t_from = __builtin_amdgcn_readfirstlane(walk.pc.t_from);
+      pc.t_to = __builtin_amdgcn_readfirstlane(walk.pc.t_to);
+      pc.n = __builtin_amdgcn_readfirstlane(walk.pc.n);
+      pc.whole = __builtin_amdgcn_readfirstlane((int)walk.pc.whole) != 0;
+      pc.first = __builtin_amdgcn_readfirstlane((int)walk.pc.first) != 0;
+      pc.slot = __builtin_amdgcn_readfirstlane(walk.pc.slot);
+      pc.v_first = __builtin_amdgcn_readfirstlane(walk.pc.v_first);
+      pc.n_parts = __builtin_amdgcn_readfirstlane(walk.pc.n_parts);
+      prefill_piece<D, MODE>(p, pc);
+      __syncthreads();  // every wave is done with the piece (and with reading the walk)
+      if (threadIdx.x == 0) split_next(p, walk);
+      __syncthreads();
     }
   }
 }
@@ -965,6 +1215,8 @@ int launch_variant(const pfa::Launch& L) {
   p.total_k = L.total_k;
   p.window = L.window;
   p.no_skip = (L.flags & PFA_FLAG_NO_SKIP) ? 1 : 0;
+  p.ws_part = nullptr;
+  p.ws_cnt = nullptr;
   p.ring = L.ring;
   p.batch = L.batch;
   p.n_qblk = (L.lq + kBM - 1) / kBM;
@@ -987,24 +1239,37 @@ int launch_variant(const pfa::Launch& L) {
   p.sel_sb = L.sel_sb;
   p.sel_sh = L.sel_sh;
   p.sel_sq = L.sel_sq;
+  const bool split = pfa::split_applies(L);
   const void* fn;
-  if (L.bias)
-    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeBias | kModeSoftcap>)
-            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeBias>);
-  else if (L.ring)
-    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeRing | kModeSoftcap>)
-            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeRing>);
-  else if (L.key_mask)
-    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeKeyMask | kModeSoftcap>)
-            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeKeyMask>);
-  else if (L.sel)
-    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeSel | kModeSoftcap>)
-            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeSel>);
-  else
-    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeSoftcap>)
-            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, 0>);
+  if (split) {
+    // key split over a fixed set of workgroups (one per compute unit of an MI355X)
+    p.ws_part = static_cast<float*>(L.workspace);
+    p.ws_cnt = reinterpret_cast<unsigned*>(static_cast<char*>(L.workspace) + pfa::split_part_bytes(L.d));
+    if (L.key_mask)
+      fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeKeyMask | kModeSoftcap, true>)
+              : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeKeyMask, true>);
+    else
+      fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeSoftcap, true>)
+              : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, 0, true>);
+  } else if (L.bias) {
+    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeBias | kModeSoftcap, false>)
+            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeBias, false>);
+  } else if (L.ring) {
+    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeRing | kModeSoftcap, false>)
+            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeRing, false>);
+  } else if (L.key_mask) {
+    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeKeyMask | kModeSoftcap, false>)
+            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeKeyMask, false>);
+  } else if (L.sel) {
+    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeSel | kModeSoftcap, false>)
+            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeSel, false>);
+  } else {
+    fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeSoftcap, false>)
+            : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, 0, false>);
+  }
+  const unsigned grid = split ? (unsigned)pfa::kSplitWorkgroups : (unsigned)n;
   hipError_t e = hipLaunchKernel(fn,
-                                 dim3((unsigned)n), dim3(kThreads), args, 0,
+                                 dim3(grid), dim3(kThreads), args, 0,
                                  static_cast<hipStream_t>(L.stream));
   return e == hipSuccess ? PFA_OK : PFA_ERR_LAUNCH;
 }
@@ -1050,6 +1315,15 @@ int launch_ring_append(const void* k_new, const void* v_new, void* k_ring, void*
 }
 
 int rows_per_block(int) { return kBM; }
+
+long long split_part_bytes(int d) {
+  const long long floats = d == 128 ? Slot<128>::kFloats : Slot<64>::kFloats;
+  return 2LL * kSplitWorkgroups * floats * 4;
+}
+
+bool split_applies(const Launch& p) {
+  return p.workspace != nullptr && p.cu_q == nullptr && p.ring == 0 && p.bias == nullptr && p.sel == nullptr;
+}
 
 long long grid_blocks(const Launch& p) {
   const long long bm = rows_per_block(p.d);

@@ -212,6 +212,36 @@ def test_decode_invalid_arguments_rejected(lib, kw, code):
     assert dcall(**kw) == code
 
 
+def wscall(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    need = pfa.prefill_workspace_bytes(a["B"], a["Hq"], a["Hkv"], a["L"], a["S"], a["D"])
+    wsb = need if a.get("wsb") is None else a["wsb"]
+    return pfa.prefill_attn_gqa_ws_raw(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["L"], a["S"], a["D"],
+                                       a["scale"], a["off"], a["window"], a["mask"], a["o"], a.get("ws", WS), wsb,
+                                       a["stream"], a.get("flags", 0))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(ws=0), 1), (dict(L=0), 2), (dict(Hq=6, Hkv=4), 3), (dict(D=96), 4),
+    (dict(off=-1, window=5), 5), (dict(scale=0.0), 10), (dict(q=Q + 2), 6), (dict(ws=WS + 8), 6),
+    (dict(wsb=0), 11), (dict(wsb=-1), 11),
+    (dict(ws=Q), 7), (dict(ws=O - 16), 7), (dict(ws=K + 64), 7), (dict(o=Q), 7),
+    (dict(flags=2), 9),
+], ids=lambda x: str(x))
+def test_prefill_ws_invalid_arguments_rejected(lib, kw, code):
+    assert wscall(**kw) == code
+
+
+def test_prefill_workspace_bytes_function(lib):
+    # FP32 partial slots of the 256 split workgroups (two each) plus one 4-byte counter per item
+    slots128 = 2 * 256 * 8 * 64 * (16 * 4 + 2) * 4
+    assert pfa.prefill_workspace_bytes(1, 56, 8, 2048, 8192, 128) == slots128 + 56 * 8 * 4
+    assert pfa.prefill_workspace_bytes(1, 4, 2, 33, 47, 64) == 2 * 256 * 8 * 64 * (16 * 2 + 2) * 4 + 16
+    for bad in [(0, 32, 8, 100, 100, 128), (1, 30, 8, 100, 100, 128), (1, 32, 8, 100, 100, 96), (1, 32, 8, 0, 100, 128)]:
+        assert pfa.prefill_workspace_bytes(*bad) == -1, bad
+
+
 def nacall(**kw):
     a = dict(DGOOD)
     a.update(kw)

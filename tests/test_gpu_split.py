@@ -1,0 +1,172 @@
+"""GPU parity of the key-split prefill (prefill_attn_gqa_ws): a fixed grid of workgroups takes equal
+shares of the (query block, key tile) space, blocks split between workgroups leave FP32 partials in
+the caller's workspace, and the last part merges them (tiny-llm Week 2 Day 5, Task 1 merge
+equations). Checked against the fp64 CPU oracle on every output element (|O_gpu - O_ref| <= 2e-2 +
+2e-2 |O_ref|, rms(err)/rms(ref) <= 1e-2), skip == NO_SKIP bit for bit, run-to-run bit identity with
+one reused workspace, and per-query-block counters left zero.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import prefill_attention_amd as pfa  # noqa: E402
+from oracle import host_workers, oracle_sdpa  # noqa: E402
+from workloads import make_inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+ATOL = RTOL = 2e-2
+RMS_RATIO = 1e-2
+DEV = "cuda:0"
+WORKERS = max(1, min(16, host_workers()))
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def check_close(got, ref, what):
+    err = np.abs(got - ref)
+    bad = err > ATOL + RTOL * np.abs(ref)
+    rms_ref = float(np.sqrt(np.mean(ref ** 2)))
+    rms_err = float(np.sqrt(np.mean(err ** 2)))
+    msg = f"{what}: max_abs={err.max():.3e} rms_err={rms_err:.3e} rms_ref={rms_ref:.3e} bad={int(bad.sum())}"
+    assert not bad.any(), msg
+    if rms_ref > 0:
+        assert rms_err <= RMS_RATIO * rms_ref, msg
+    return msg
+
+
+def workspace_for(q_shape, k_shape):
+    B, Hq, L, D = q_shape
+    need = pfa.prefill_workspace_bytes(B, Hq, k_shape[1], L, k_shape[2], D)
+    assert need > 0
+    return torch.zeros(need, dtype=torch.uint8, device=DEV)
+
+
+def counters_zero(ws, shape):
+    """The per-query-block counters of a call on q of this shape, after its FP32 partial slots."""
+    B, Hq, L, D = shape
+    part = 2 * 256 * 8 * 64 * (16 * (D // 32) + 2) * 4
+    return bool(torch.all(ws[part:part + 4 * B * Hq * ((L + 255) // 256)] == 0))
+
+
+def run(x, ws, no_skip=False, softcap=0.0, sinks=None):
+    q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    mask = torch.from_numpy(x["key_mask"]).to(DEV) if x.get("key_mask") is not None else None
+    off = x["causal_offset"]
+    st = None if sinks is None else torch.from_numpy(sinks).to(DEV)
+    out = pfa.prefill_attn_gqa(q, k, v, scale=float(x["scale"]), causal=off >= 0,
+                               causal_offset=off if off >= 0 else None, window=x["window"], key_mask=mask,
+                               no_skip=no_skip, softcap=softcap, sinks=st, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name", ["mid_ctx_8k", "long_ctx_32k", "bidir_padded_b8", "sliding_w1024_d64"])
+def test_split_full_size(name):
+    x = make_inputs(name, seed=0)
+    ws = workspace_for(x["q"].shape, x["k"].shape)
+    print(f"[split] {name}", flush=True)
+    a = run(x, ws)
+    assert counters_zero(ws, x["q"].shape)
+    b = run(x, ws)                 # the same workspace again: counters were left zero
+    n = run(x, ws, no_skip=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run to run"
+    assert torch.equal(a.view(torch.int16), n.view(torch.int16)), "skip == no-skip"
+    got = a.double().cpu().numpy()
+    del a, b, n
+    ref = oracle_sdpa(x["q"], x["k"], x["v"], x["scale"], x["causal_offset"], x["window"], x["key_mask"],
+                      workers=WORKERS)
+    print(check_close(got, ref, name), flush=True)
+
+
+# fewer query blocks than compute units, the shapes the split is for: 8 query heads on one KV head,
+# a 2048-row chunk after 30720 cached keys (64 blocks); 8 heads on 2 KV heads, 512 rows after 65024
+# keys at D = 64 (16 blocks, each cut into 16 parts)
+FEW_BLOCKS = {
+    "h8_kv1_32k": dict(B=1, Hq=8, Hkv=1, D=128, L=2048, S=32768, causal_offset=30720, window=0, amp=1.0,
+                       key_padding=None),
+    "h8_kv2_64k_d64": dict(B=1, Hq=8, Hkv=2, D=64, L=512, S=65536, causal_offset=65024, window=0, amp=1.0,
+                           key_padding=None),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FEW_BLOCKS))
+def test_split_few_blocks(name):
+    x = make_inputs(FEW_BLOCKS[name], seed=5)
+    ws = workspace_for(x["q"].shape, x["k"].shape)
+    print(f"[split few blocks] {name}", flush=True)
+    a = run(x, ws)
+    assert counters_zero(ws, x["q"].shape)
+    b = run(x, ws)
+    n = run(x, ws, no_skip=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run to run"
+    assert torch.equal(a.view(torch.int16), n.view(torch.int16)), "skip == no-skip"
+    got = a.double().cpu().numpy()
+    del a, b, n
+    ref = oracle_sdpa(x["q"], x["k"], x["v"], x["scale"], x["causal_offset"], x["window"], x["key_mask"],
+                      workers=WORKERS)
+    print(check_close(got, ref, name), flush=True)
+
+
+def random_cases(n=32, seed=91):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2, 8]))
+        G = int(rng.choice([1, 2, 4, 7]))
+        B = int(rng.integers(1, 4))
+        D = int(rng.choice([64, 128]))
+        L = int(rng.integers(1, 1400))
+        S = int(rng.integers(1, 3000))
+        kind = i % 4
+        if kind == 0:
+            off, W = S - L if S >= L else int(rng.integers(0, S + 1)), 0
+        elif kind == 1:
+            off, W = int(rng.integers(0, S + 200)), int(rng.choice([1, 5, 64, 300]))   # windows, some past S
+        elif kind == 2:
+            off, W = -1, 0
+        else:
+            off, W = max(0, S - L), int(rng.integers(1, 2000))
+        kp = (1, S) if (i % 3 == 0 and S > 1) else None
+        out.append(dict(B=B, Hq=Hkv * G, Hkv=Hkv, D=D, L=L, S=S, causal_offset=off, window=W, amp=1.0,
+                        key_padding=kp))
+    return out
+
+
+def test_split_random_shapes_one_workspace():
+    """Ragged shapes (tails on both axes, windows that start past the last key, key padding,
+    bidirectional, D = 64 and 128, fewer key tiles than workgroups) with soft-cap and sinks on some,
+    all through one workspace sized for the largest: oracle parity, skip == no-skip bitwise,
+    counters zero after every call."""
+    cases = random_cases()
+    need = max(pfa.prefill_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["S"], c["D"]) for c in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for i, c in enumerate(cases):
+        x = make_inputs(c, seed=100 + i)
+        softcap = 30.0 if i % 5 == 1 else 0.0
+        sinks = (np.random.default_rng(i).standard_normal(c["Hq"]) * 2).astype(np.float32) if i % 4 == 3 else None
+        print(f"[split random] {i} {c} softcap={softcap} sinks={sinks is not None}", flush=True)
+        a = run(x, ws, softcap=softcap, sinks=sinks)
+        n = run(x, ws, no_skip=True, softcap=softcap, sinks=sinks)
+        assert torch.equal(a.view(torch.int16), n.view(torch.int16)), f"case {i}: skip == no-skip"
+        assert counters_zero(ws, x["q"].shape)
+        ref = oracle_sdpa(x["q"], x["k"], x["v"], x["scale"], x["causal_offset"], x["window"], x["key_mask"],
+                          workers=WORKERS, softcap=softcap, sinks=None if sinks is None else sinks.astype(np.float64))
+        got = a.double().cpu().numpy()
+        check_close(got, ref, f"case {i}")
+        empty = ~np.any(np.abs(ref) > 0, axis=-1)
+        assert np.all(got[empty] == 0.0), f"case {i}: rows without keys are zeros"
+
+
+def test_split_close_to_per_item_grid():
+    # another summation boundary, so not bitwise; both within the oracle tolerance of each other
+    x = make_inputs("mid_ctx_8k", seed=3)
+    q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    ws = workspace_for(tuple(q.shape), tuple(k.shape))
+    a = pfa.prefill_attn_gqa(q, k, v, scale=float(x["scale"]), causal_offset=x["causal_offset"], workspace=ws)
+    b = pfa.prefill_attn_gqa(q, k, v, scale=float(x["scale"]), causal_offset=x["causal_offset"])
+    torch.cuda.synchronize()
+    check_close(a.double().cpu().numpy(), b.double().cpu().numpy(), "split vs per-item grid")
