@@ -185,17 +185,19 @@ int prefill_attn_gqa_opt(const void* Q, const void* K, const void* V,
  * PFA_FLAG_NO_SKIP; they may differ in the last bits from prefill_attn_gqa (other summation
  * boundaries). Both meet the same tolerance.
  *
- * When it pays: with B * Hq * ceil(L / 256) well below 256. With a few hundred blocks or more,
- * prefill_attn_gqa is faster: its workgroups start together at the first key tile and walk the
- * keys in step, so the K / V tiles of a KV head are fetched once per L2, while the shares of a
+ * The split is taken only where it pays, when B * Hq * ceil(L / 256) <= 192 (three quarters of
+ * the grid). With more blocks, and with an additive bias or a block bitmap, the call runs exactly as
+ * prefill_attn_gqa_opt (bit-identical results) and leaves the workspace untouched: one workgroup
+ * per block is then faster, since those workgroups start together at the first key tile and walk
+ * the keys in step (each K / V tile of a KV head is fetched once per L2), while the shares of a
  * split start at scattered key tiles.
  *
  * Same arguments as prefill_attn_gqa_opt, plus a DEVICE workspace of at least
  * pfa_prefill_workspace_bytes(B, Hq, Hkv, L, S, D) bytes, 16-byte aligned, not overlapping any
  * other buffer of the call, ZERO-FILLED before its first use (it holds one counter per query block,
  * and every call leaves the counters zero again). Calls that share a workspace must be ordered on
- * one stream. With an additive bias or a block bitmap the call runs as prefill_attn_gqa_opt and
- * leaves the workspace untouched. Returns a pfa_status code (PFA_ERR_WORKSPACE if it is too small).
+ * one stream. Returns a pfa_status code (PFA_ERR_WORKSPACE if the workspace is too small, checked
+ * whether or not the split is taken).
  */
 int prefill_attn_gqa_ws(const void* Q, const void* K, const void* V,
                         int B, int Hq, int Hkv, int L, int S, int D,

@@ -54,8 +54,9 @@ constexpr int kSplitWorkgroups = 256;
 // Bytes of FP32 partial slots a key-split launch uses (two per workgroup), before the counters.
 long long split_part_bytes(int d);
 
-// Whether launch_prefill runs the key split for this call (a workspace is given and the layout is
-// the dense one without bias, block bitmap or rotating cache).
+// Whether launch_prefill runs the key split for this call: a workspace is given, the layout is the
+// dense one without bias, block bitmap or rotating cache, and the call has at most 3/4 as many
+// query blocks as the split has workgroups (with more, one workgroup per block is faster).
 bool split_applies(const Launch& p);
 
 // Query rows handled by one workgroup of the prefill kernel.

@@ -67,9 +67,9 @@ constexpr int kXcds = 8;
 constexpr int kRing = 4;  // LDS operands in flight in the MFMA phase
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
-constexpr float kLazyLog2 = 8.0f;
+constexpr float kLazyLog2 = 8.0f;  // reference-max slack of the lazy rescale (P <= 2^8)
 // dword 3 of a raw buffer descriptor (32-bit data format, no swizzle, bounds checked per byte)
-constexpr int kBufferFlags = 0x00020000;  // reference-max slack of the lazy rescale (P <= 2^8)
+constexpr int kBufferFlags = 0x00020000;
 
 // sched_group_barrier masks
 constexpr int kSchedMfma = 0x008;
@@ -295,12 +295,15 @@ struct Piece {
 // (it starts inside it), 2v + 1 for a part that starts an item and ends inside it.
 __device__ __forceinline__ int part_slot(int v, bool starts_item) { return 2 * v + (starts_item ? 1 : 0); }
 
-// Device-coherent (agent-scope) FP32 store and load of a key-split partial.
-__device__ __forceinline__ void store_coherent(float* a, float x) {
-  __hip_atomic_store(a, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Device-coherent FP32 accesses to the key split's partials: buffer loads and stores with the SC1
+// cache-policy bit (agent scope), which go through to the memory side past the per-XCD L2s. They
+// are ordinary (non-atomic) accesses, so many are in flight at once.
+constexpr int kCoherent = 16;  // SC1
+__device__ __forceinline__ void part_store(__amdgpu_buffer_rsrc_t r, unsigned off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, off, 0, kCoherent);
 }
-__device__ __forceinline__ float load_coherent(const float* a) {
-  return __hip_atomic_load(const_cast<float*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ float part_load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCoherent));
 }
 
 template <int D>
@@ -310,7 +313,7 @@ struct Slot {
 };
 
 template <int D, int MODE>
-__device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc) {
+__device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, const int tid) {
   constexpr bool KMASK = (MODE & kModeKeyMask) != 0;
   constexpr bool RING = (MODE & kModeRing) != 0;
   constexpr bool SOFTCAP = (MODE & kModeSoftcap) != 0;
@@ -330,7 +333,6 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc) 
   __shared__ __attribute__((aligned(1024))) char lds_raw[kStages * G::kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t m_lds[kStages][kBN];
 
-  const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
@@ -985,48 +987,53 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc) 
   if (!pc.whole) {
     using SL = Slot<D>;
     __shared__ int s_last;
-    float* mine = p.ws_part + (size_t)pc.slot * SL::kFloats + (size_t)wave * SL::kRegs * 64 + lane;
+    // the partial slots: 2 per workgroup of the split, each lane's values 64 floats apart
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        p.ws_part, 0, 2 * pfa::kSplitWorkgroups * SL::kFloats * 4, kBufferFlags);
+    auto part_base = [&](int slot) -> unsigned {
+      return ((unsigned)slot * SL::kFloats + (unsigned)(wave * SL::kRegs * 64 + lane)) * 4u;
+    };
+    const unsigned mine = part_base(pc.slot);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) store_coherent(mine + (16 * db + v) * 64, acc[db][v]);
-    store_coherent(mine + (16 * DB) * 64, mref);
-    store_coherent(mine + (16 * DB + 1) * 64, l_run);
-    // Partials are written and read with device-coherent accesses (through to the memory side,
-    // past the per-XCD L2s) instead of a device-wide fence: such a fence writes back and
-    // invalidates this XCD's whole L2, which the other workgroups there are streaming K / V
-    // through. Every store has completed before the count is raised, and the last part's loads
-    // are issued only after its count has returned.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      for (int v = 0; v < 16; ++v) part_store(rs, mine + (16 * db + v) * 256, acc[db][v]);
+    part_store(rs, mine + (16 * DB) * 256, mref);
+    part_store(rs, mine + (16 * DB + 1) * 256, l_run);
+    // Partials are written and read with device-coherent accesses instead of a device-wide fence
+    // (which writes back and invalidates this XCD's whole L2, where the other workgroups stream
+    // K / V). Every store has completed before the count is raised (the asm also keeps the
+    // compiler from moving a store past it), and the last part's loads are issued only after its
+    // count has returned.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) s_last = atomicAdd(&p.ws_cnt[pc.item], 1u) + 1u == (unsigned)pc.n_parts;
     __syncthreads();
     if (!s_last) return;
     // merge the parts in their key order, whichever finished last: the merge equations (tiny-llm
-    // Task 1) on (reference max, sum, accumulator), in the base-2 domain
-    mref = -INFINITY;
+    // Task 1) on (reference max, sum, accumulator) in the base-2 domain, taken against the largest
+    // reference of the parts; a part without visible keys (reference -inf, sum 0, zero
+    // accumulator) gets weight 0
+    float mm = -INFINITY;
+    for (int k = 0; k < pc.n_parts; ++k)
+      mm = max2(mm, part_load(rs, part_base(part_slot(pc.v_first + k, k == 0)) + (16 * DB) * 256));
     l_run = 0.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[db][v] = 0.0f;
     for (int k = 0; k < pc.n_parts; ++k) {
-      const int sl = part_slot(pc.v_first + k, k == 0);
-      const float* src = p.ws_part + (size_t)sl * SL::kFloats + (size_t)wave * SL::kRegs * 64 + lane;
-      const float mk = load_coherent(src + (16 * DB) * 64);
-      const float lk = load_coherent(src + (16 * DB + 1) * 64);
-      const float mn = max2(mref, mk);
-      // a part without visible keys (mk = -inf, lk = 0, zero accumulator) changes nothing; while
-      // both are -inf the factors stay 1 (no -inf - -inf)
-      const float a0 = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref - mn);
-      const float a1 = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mk - mn);
-      l_run = l_run * a0 + lk * a1;
+      const unsigned src = part_base(part_slot(pc.v_first + k, k == 0));
+      const float mk = part_load(rs, src + (16 * DB) * 256);
+      const float w = (mk == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mk - mm);
+      l_run = __builtin_fmaf(part_load(rs, src + (16 * DB + 1) * 256), w, l_run);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[db][v] = acc[db][v] * a0 + load_coherent(src + (16 * db + v) * 64) * a1;
-      mref = mn;
+        for (int v = 0; v < 16; ++v)
+          acc[db][v] = __builtin_fmaf(part_load(rs, src + (16 * db + v) * 256), w, acc[db][v]);
     }
+    mref = mm;
     if (tid == 0) __hip_atomic_store(&p.ws_cnt[pc.item], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
   }
 
@@ -1064,6 +1071,7 @@ struct SplitWalk {
   long long pos, r1;               // next tile of the share, end of the share
   int hk, qrank, n, nb, Pe, v;
   int done;
+  int zero;  // 0, read again for every piece (see the piece loop)
   Piece pc;
 };
 
@@ -1121,6 +1129,7 @@ __device__ __forceinline__ void split_init(const Params& p, SplitWalk& w) {
   // and the parts of an item are consecutive workgroups
   w.Pe = (int)(w.T < P ? w.T : P);
   w.done = 0;
+  w.zero = 0;
   if (w.v >= w.Pe) {
     w.done = 1;
     return;
@@ -1167,7 +1176,7 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     pc.item = item;
     pc.whole = true;
     pc.first = true;
-    prefill_piece<D, MODE>(p, pc);
+    prefill_piece<D, MODE>(p, pc, (int)threadIdx.x);
   } else {
     // key split (dense layout): a fixed grid, each workgroup its share of the linear space
     __shared__ SplitWalk walk;
@@ -1185,7 +1194,10 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
       pc.slot = __builtin_amdgcn_readfirstlane(walk.pc.slot);
       pc.v_first = __builtin_amdgcn_readfirstlane(walk.pc.v_first);
       pc.n_parts = __builtin_amdgcn_readfirstlane(walk.pc.n_parts);
-      prefill_piece<D, MODE>(p, pc);
+      // the thread index plus a zero the compiler cannot see through: everything a piece derives
+      // from the lane (LDS and global addresses) is then computed per piece instead of being
+      // hoisted out of this loop, where it would stay live through every piece's merge
+      prefill_piece<D, MODE>(p, pc, (int)threadIdx.x + walk.zero);
       __syncthreads();  // every wave is done with the piece (and with reading the walk)
       if (threadIdx.x == 0) split_next(p, walk);
       __syncthreads();
@@ -1322,7 +1334,8 @@ long long split_part_bytes(int d) {
 }
 
 bool split_applies(const Launch& p) {
-  return p.workspace != nullptr && p.cu_q == nullptr && p.ring == 0 && p.bias == nullptr && p.sel == nullptr;
+  return p.workspace != nullptr && p.cu_q == nullptr && p.ring == 0 && p.bias == nullptr && p.sel == nullptr &&
+         grid_blocks(p) * 4 <= 3LL * kSplitWorkgroups;
 }
 
 long long grid_blocks(const Launch& p) {
