@@ -60,6 +60,8 @@ WORKLOADS = {
     "decode_b8_l1_4k": ["decode_b8_l1_4k"],
     "long_ctx_32k_sinks": ["long_ctx_32k_sinks"],
     "long_ctx_32k_sel": ["long_ctx_32k_sel"],
+    "few_heads_32k": ["few_heads_32k"],
+    "few_heads_32k_split": ["few_heads_32k_split"],
 }
 DESCRIPTION = {
     "causal_8k_32k": "causal GQA prefill chunks, L=2048 on S=8192 (Hq=56,Hkv=8) and on S=32768 "
@@ -242,25 +244,28 @@ def cpu_baseline(workload: str, workers: int, budget_s: float = 20.0) -> dict:
 
 def kernel_name(workload_name: str) -> str:
     """Name of the dominant kernel as rocprofv3 prints it (prefill MODE bits: 1 key mask, 2 ring,
-    4 soft-cap, 8 bias, 16 block bitmap)."""
+    4 soft-cap, 8 bias, 16 block bitmap; the last argument is true for the key split)."""
     from workloads import CONFIGS, VARLEN_CONFIGS
 
     if workload_name in VARLEN_CONFIGS:
-        return "pfa_prefill_kernel<%d, 0>" % VARLEN_CONFIGS[workload_name]["D"]
+        return "pfa_prefill_kernel<%d, 0, false>" % VARLEN_CONFIGS[workload_name]["D"]
     c = CONFIGS[workload_name]
     if c.get("entry") == "decode":
         rows = (c["Hq"] // c["Hkv"]) * c["L"]
         sc = "true" if c.get("softcap") else "false"
-        if rows <= 32 and not c["key_padding"]:
+        # up to 64 rows per KV head in 32-row groups (the register-K kernel without a key mask),
+        # more in 64-row groups
+        if rows <= 64 and not c["key_padding"]:
             split = "pfa_decode_kreg_kernel<%d, %s>" % (c["D"], sc)
         else:
             split = "pfa_decode_split_kernel<%d, %d, %s, %s>" % (
-                c["D"], 2 if rows > 32 else 1, "true" if c["key_padding"] else "false", sc)
+                c["D"], 2 if rows > 64 else 1, "true" if c["key_padding"] else "false", sc)
         return "%s + pfa_decode_merge_kernel<%d>" % (split, c["D"])
     mode = (1 if c["key_padding"] else 0) | (2 if c.get("entry") == "ring" else 0) | \
         (4 if c.get("softcap") else 0) | (8 if c.get("bias") else 0) | (16 if c.get("block_sel") else 0)
     suffix = " (after pfa_ring_append_kernel)" if c.get("entry") == "ring" else ""
-    return "pfa_prefill_kernel<%d, %d>%s" % (c["D"], mode, suffix)
+    split = "true" if c.get("entry") == "split" else "false"
+    return "pfa_prefill_kernel<%d, %d, %s>%s" % (c["D"], mode, split, suffix)
 
 
 def varlen_cpu_baseline(name: str, workers: int, budget_s: float = 20.0) -> dict:
@@ -377,6 +382,10 @@ def main() -> int:
             kw.update(block_sel=torch.from_numpy(x["block_sel"]).to(dev), block_q=x["block_q"], block_k=x["block_k"])
         if c.get("entry") == "decode":
             kw["workspace"] = torch.empty(pfa.decode_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["S"], c["D"]),
+                                          dtype=torch.uint8, device=dev)
+        if c.get("entry") == "split":
+            # zero-filled once: the key split leaves its counters zero after every call
+            kw["workspace"] = torch.zeros(pfa.prefill_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["S"], c["D"]),
                                           dtype=torch.uint8, device=dev)
         if x.get("block_sel") is not None:
             flops = 4 * c["D"] * sel_visible_pairs(c, x["block_sel"], x["block_q"], x["block_k"])

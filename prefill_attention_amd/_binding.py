@@ -129,9 +129,11 @@ def prefill_attn_gqa_ws_raw(q_ptr: int, k_ptr: int, v_ptr: int, B: int, Hq: int,
                             S: int, D: int, scale: float, causal_offset: int, window: int,
                             key_mask_ptr: int | None, o_ptr: int, ws_ptr: int | None, ws_bytes: int,
                             stream: int | None, flags: int = 0, softcap: float = 0.0,
-                            sinks_ptr: int | None = None) -> int:
+                            sinks_ptr: int | None = None, bias_ptr: int | None = None, bias_strides=(0, 0, 0),
+                            sel_ptr: int | None = None, sel_blocks=(0, 0), sel_strides=(0, 0, 0)) -> int:
     """Direct C-ABI call of the key-split prefill entry point; returns the status code."""
-    opts = Options(flags, softcap, None, 0, 0, 0, sinks_ptr or None)
+    opts = Options(flags, softcap, bias_ptr or None, *bias_strides, sinks_ptr or None, sel_ptr or None,
+                   *sel_blocks, *sel_strides)
     return int(library().prefill_attn_gqa_ws(
         q_ptr, k_ptr, v_ptr, B, Hq, Hkv, L, S, D, ctypes.c_float(scale), causal_offset, window,
         key_mask_ptr or None, o_ptr, ws_ptr or None, ws_bytes, stream or None, ctypes.byref(opts)))
@@ -255,8 +257,6 @@ def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True
     if workspace is not None:
         # the key-split entry point (prefill_attn_gqa_ws): a zero-filled uint8 GPU tensor of at least
         # prefill_workspace_bytes(...) bytes, reused by calls ordered on one stream
-        if bias is not None or block_sel is not None:
-            raise ValueError("the workspace (key-split) call takes no bias or block bitmap")
         if (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or workspace.device != q.device
                 or not workspace.is_contiguous()):
             raise ValueError(f"workspace must be a contiguous uint8 tensor on {q.device}")
@@ -264,7 +264,8 @@ def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True
             rc = prefill_attn_gqa_ws_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, S, D,
                                          float(scale), int(causal_offset), int(window), mask_ptr, out.data_ptr(),
                                          workspace.data_ptr(), workspace.numel(), stream_ptr,
-                                         FLAG_NO_SKIP if no_skip else 0, float(softcap), sinks_ptr)
+                                         FLAG_NO_SKIP if no_skip else 0, float(softcap), sinks_ptr,
+                                         bias_ptr, bias_strides, sel_ptr, (int(block_q), int(block_k)), sel_strides)
         if rc != 0:
             raise PfaError(rc, status_str(rc))
         return out

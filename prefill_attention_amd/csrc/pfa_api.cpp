@@ -314,14 +314,20 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int L, int S, int D) {
   // four 32-key tiles per split; with at most 32 rows per KV head (the register-K kernel, whose
   // waves stream the keys fastest) at least twelve, which halves the partials the merge reads and
   // still leaves about 700 workgroups for one-token decode on a 32K cache (15 % faster per call
-  // than four; the 64-row kernel needs the smaller splits to fill the chip)
+  // than four; the 64-row kernel needs the smaller splits to fill the chip); with two 32-row groups
+  // per KV head at least eight (measured on 56 rows of 8K keys per KV head: 22.4 us per call
+  // against 23.6 with twelve and 25.4 with four, whose partials the merge reads twice over)
   constexpr long long kTargetGroups = 1280;
   constexpr long long kMinTilesPerSplit = 4;
   constexpr long long kMinTilesPerSplitFewRows = 12;
+  constexpr long long kMinTilesPerSplitTwoGroups = 8;
   DecodePlan pl;
   const long long R = static_cast<long long>(Hq / Hkv) * L;
-  pl.n_rowgrp = static_cast<int>((R + 63) / 64);
-  pl.rows_cap = static_cast<int>(R < 64 ? R : 64);
+  // up to 64 rows per KV head go in groups of 32 (the one-block kernels, the register-K one
+  // without a key mask), each group streaming the keys itself; more in groups of 64 (two blocks)
+  pl.rows_per_group = R <= 64 ? 32 : 64;
+  pl.n_rowgrp = static_cast<int>((R + pl.rows_per_group - 1) / pl.rows_per_group);
+  pl.rows_cap = static_cast<int>(R < pl.rows_per_group ? R : pl.rows_per_group);
   const long long tiles = (static_cast<long long>(S) + 31) / 32;
   const long long units = static_cast<long long>(B) * Hkv * pl.n_rowgrp;
   long long n_split = (kTargetGroups + units - 1) / units;
@@ -329,11 +335,15 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int L, int S, int D) {
   if (n_split < 1) n_split = 1;
   long long tps = (tiles + n_split - 1) / n_split;
   if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
-  if (pl.rows_cap <= 32 && tps < kMinTilesPerSplitFewRows) tps = kMinTilesPerSplitFewRows;
+  if (pl.rows_per_group == 32) {
+    const long long few = pl.n_rowgrp == 1 ? kMinTilesPerSplitFewRows : kMinTilesPerSplitTwoGroups;
+    if (tps < few) tps = few;
+  }
   n_split = (tiles + tps - 1) / tps;
   pl.n_split = static_cast<int>(n_split);
   pl.tiles_per_split = static_cast<int>(tps);
   pl.n_partials = units * n_split;
+  pl.grid = pl.rows_per_group == 32 ? (units / pl.n_rowgrp * n_split + 7) / 8 * 8 * pl.n_rowgrp : pl.n_partials;
   pl.workspace_bytes = pl.n_partials * pl.rows_cap * (static_cast<long long>(D) + 2) * 4;
   return pl;
 }
@@ -449,7 +459,7 @@ static int decode_call(const void* Q, const void* K, const void* V, int B, int H
   if (!library_scratch && !workspace) return PFA_ERR_NULL;
   if (L > PFA_DECODE_MAX_L || B > (1 << 20) || Hq > (1 << 20)) return PFA_ERR_SIZE;
   const pfa::DecodePlan plan = pfa::decode_plan(B, Hq, Hkv, L, S, D);
-  if (plan.n_partials > INT_MAX || static_cast<long long>(B) * Hq * L > INT_MAX) return PFA_ERR_SIZE;
+  if (plan.grid > INT_MAX || static_cast<long long>(B) * Hq * L > INT_MAX) return PFA_ERR_SIZE;
   const auto bytes = [](long long a, long long b, long long c, long long d) {
     return static_cast<uintptr_t>(a) * static_cast<uintptr_t>(b) * static_cast<uintptr_t>(c) *
            static_cast<uintptr_t>(d) * 2u;

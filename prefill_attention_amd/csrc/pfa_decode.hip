@@ -42,7 +42,6 @@ constexpr int kTk = 32;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor dword 3: 32-bit format, per-byte bounds
-constexpr int kRowsPerGroup = 64;          // query rows of one workgroup (two 32-row MFMA blocks)
 
 template <int D>
 struct DGeo {
@@ -70,8 +69,46 @@ struct DParams {
   float sc_inv, sc_cap_l2;  // logit soft-capping: scale / cap and cap * log2(e)
   const float* sinks;       // null, or fp32 [hq] sink logits (an extra normaliser term per row)
   int n_rowgrp, rows_cap, n_split, tiles_per_split;
+  int rows_per_group;  // 32 (one MFMA block per wave) or 64 (two)
+  int xcd_pairs;       // workgroup order of the 32-row kernels (decode_unit)
   long long n_partials;
 };
+
+// Workgroup -> (b, kv head, row group, split) and its partial index ((b * hkv + hk) * n_rowgrp +
+// rg) * n_split + split, the numbering the merge kernel reads. The 64-row kernel numbers the
+// workgroups like its partials (splits of one row group adjacent). The 32-row kernels deal the
+// row groups of one (b, kv head, split) 8 workgroups apart: the hardware deals workgroups to the 8
+// XCDs round-robin, so they run on one XCD at about the same time and the later ones find the K / V
+// tiles in its L2. That grid is padded to a multiple of 8 per row group; padding workgroups get
+// valid = false.
+struct DecodeUnit {
+  int b, hk, rg, split;
+  long long part;
+  bool valid;
+};
+__device__ __forceinline__ DecodeUnit decode_unit(const DParams& p) {
+  DecodeUnit u;
+  long long id = blockIdx.x;
+  u.valid = true;
+  if (p.xcd_pairs) {
+    const int lane8 = (int)(id % 8);
+    id /= 8;
+    u.rg = (int)(id % p.n_rowgrp);
+    id = id / p.n_rowgrp * 8 + lane8;  // the (b, kv head, split) unit, split fastest
+    u.valid = id < p.n_partials / p.n_rowgrp;
+    u.split = (int)(id % p.n_split);
+    id /= p.n_split;
+  } else {
+    u.split = (int)(id % p.n_split);
+    id /= p.n_split;
+    u.rg = (int)(id % p.n_rowgrp);
+    id /= p.n_rowgrp;
+  }
+  u.hk = (int)(id % p.hkv);
+  u.b = (int)(id / p.hkv);
+  u.part = (((long long)u.b * p.hkv + u.hk) * p.n_rowgrp + u.rg) * p.n_split + u.split;
+  return u;
+}
 
 __device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
@@ -115,15 +152,11 @@ __global__ __launch_bounds__(64, (RB == 1 ? 2 : 1)) void pfa_decode_split_kernel
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // ---- workgroup -> (b, kv head, row group, split); splits of one (b, hk, rg) are adjacent ----
-  long long id = blockIdx.x;
-  const int split = (int)(id % p.n_split);
-  id /= p.n_split;
-  const int rg = (int)(id % p.n_rowgrp);
-  id /= p.n_rowgrp;
-  const int hk = (int)(id % p.hkv);
-  const int b = (int)(id / p.hkv);
-  const long long part = blockIdx.x;  // partial index (same numbering as the workgroups)
+  // ---- workgroup -> (b, kv head, row group, split) ----
+  const DecodeUnit u = decode_unit(p);
+  if (!u.valid) return;
+  const int split = u.split, rg = u.rg, hk = u.hk, b = u.b;
+  const long long part = u.part;
   const int L = p.lq, S = p.sk;
   const int R = p.group * L;  // rows of this KV head: (g, i) -> g * L + i
 
@@ -133,7 +166,7 @@ __global__ __launch_bounds__(64, (RB == 1 ? 2 : 1)) void pfa_decode_split_kernel
   int grp_lo = S, grp_hi = -1;  // union over the workgroup's real rows (wave-uniform after reduction)
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int r = rg * kRowsPerGroup + rb * 32 + l32;
+    const int r = rg * p.rows_per_group + rb * 32 + l32;
     int lo = S, hi = -1;  // empty
     if (r < R) {
       const int g = r / L, i = r % L;
@@ -388,21 +421,20 @@ __global__ __launch_bounds__(64, 2) void pfa_decode_kreg_kernel(DParams p) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // ---- workgroup -> (b, kv head, split): one row group (rows_cap <= 32) ----
-  long long id = blockIdx.x;
-  const int split = (int)(id % p.n_split);
-  id /= p.n_split;
-  const int hk = (int)(id % p.hkv);
-  const int b = (int)(id / p.hkv);
-  const long long part = blockIdx.x;
+  // ---- workgroup -> (b, kv head, row group of 32 rows, split) ----
+  const DecodeUnit u = decode_unit(p);
+  if (!u.valid) return;
+  const int split = u.split, hk = u.hk, b = u.b;
+  const long long part = u.part;
   const int L = p.lq, S = p.sk;
   const int R = p.group * L;
 
   // ---- this lane's row and its visible key interval [lo, hi] ----
   bf16x8 qreg[KQ];
   int lo = S, hi = -1;  // empty
-  if (l32 < R) {
-    const int g = l32 / L, i = l32 % L;
+  const int r = u.rg * 32 + l32;
+  if (r < R) {
+    const int g = r / L, i = r % L;
     const uint16_t* qrow = p.q + (((long long)b * p.hq + hk * p.group + g) * L + i) * (long long)D;
 #pragma unroll
     for (int kk = 0; kk < KQ; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * hh);
@@ -621,7 +653,7 @@ __global__ __launch_bounds__(kMergeThreads) void pfa_decode_merge_kernel(DParams
   const int b = (int)(id / p.hq);
   const int hk = h / p.group, g = h % p.group;
   const int r = g * p.lq + i;
-  const int rg = r / kRowsPerGroup, rr = r % kRowsPerGroup;
+  const int rg = r / p.rows_per_group, rr = r % p.rows_per_group;
   const long long part0 = (((long long)b * p.hkv + hk) * p.n_rowgrp + rg) * p.n_split;
   const float* ws_ml = p.ws + (size_t)p.n_partials * p.rows_cap * D;
   // local merge of this thread's splits (empty splits have m = -inf and l = a = 0)
@@ -719,6 +751,8 @@ int launch_decode_variant(const pfa::Launch& L, const pfa::DecodePlan& plan, voi
   p.n_split = plan.n_split;
   p.tiles_per_split = plan.tiles_per_split;
   p.n_partials = plan.n_partials;
+  p.rows_per_group = plan.rows_per_group;
+  p.xcd_pairs = plan.rows_per_group == 32 ? 1 : 0;
   hipStream_t stream = static_cast<hipStream_t>(L.stream);
   void* args[] = {&p};
   const void* fn =
@@ -729,7 +763,7 @@ int launch_decode_variant(const pfa::Launch& L, const pfa::DecodePlan& plan, voi
                        : reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, true, false>))
                  : (sc ? reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, false, true>)
                        : reinterpret_cast<const void*>(&pfa_decode_split_kernel<D, RB, false, false>));
-  if (hipLaunchKernel(fn, dim3((unsigned)plan.n_partials), dim3(64), args, 0, stream) != hipSuccess)
+  if (hipLaunchKernel(fn, dim3((unsigned)plan.grid), dim3(64), args, 0, stream) != hipSuccess)
     return PFA_ERR_LAUNCH;
   uint16_t* o = static_cast<uint16_t*>(L.o);
   void* margs[] = {&p, &o};

@@ -73,12 +73,14 @@ int launch_ring_append(const void* k_new, const void* v_new, void* k_ring, void*
                        int D, int ring, int pos0, void* stream);
 
 // Work split of the short-query (decode) path, a pure function of the shape so that the
-// workspace query and the launch agree: the rows of one KV head (G * L) in row groups of up to 64,
-// the keys in n_split ranges of tiles_per_split 32-key tiles, one partial per
-// (b, kv head, row group, split).
+// workspace query and the launch agree: the rows of one KV head (G * L) in row groups of
+// rows_per_group rows (32 when G * L <= 64, else 64), the keys in n_split ranges of
+// tiles_per_split 32-key tiles, one partial per (b, kv head, row group, split).
 struct DecodePlan {
   int n_rowgrp = 0;
-  int rows_cap = 0;  // rows stored per partial: min(G * L, 64)
+  int rows_per_group = 0;
+  int rows_cap = 0;  // rows stored per partial: min(G * L, rows_per_group)
+  long long grid = 0;  // workgroups of the split kernel (32-row groups: padded, see decode_unit)
   int n_split = 0;
   int tiles_per_split = 0;
   long long n_partials = 0;

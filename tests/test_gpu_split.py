@@ -87,6 +87,31 @@ def test_many_blocks_run_the_per_item_grid(name):
     assert not bool(torch.any(ws != 0)), "workspace untouched"
 
 
+@pytest.mark.parametrize("opt", ["bias", "block_sel"])
+def test_bias_or_bitmap_run_the_per_item_grid(opt):
+    """The workspace call with an additive bias or a block bitmap is the per-item call, also for a
+    shape within the split limit."""
+    c = dict(B=1, Hq=8, Hkv=2, D=128, L=600, S=1500, causal_offset=900, window=0, amp=1.0, key_padding=None)
+    if opt == "bias":
+        c["bias"] = "LS"
+    else:
+        c["block_sel"] = dict(block_q=64, block_k=128, density=0.5)
+    x = make_inputs(c, seed=11)
+    assert n_blocks(x) <= SPLIT_MAX_BLOCKS
+    q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    kw = dict(scale=float(x["scale"]), causal_offset=x["causal_offset"])
+    if opt == "bias":
+        kw["bias"] = torch.from_numpy(x["bias"]).to(DEV)
+    else:
+        kw.update(block_sel=torch.from_numpy(x["block_sel"]).to(DEV), block_q=x["block_q"], block_k=x["block_k"])
+    ws = workspace_for(tuple(q.shape), tuple(k.shape))
+    a = pfa.prefill_attn_gqa(q, k, v, workspace=ws, **kw)
+    b = pfa.prefill_attn_gqa(q, k, v, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert not bool(torch.any(ws != 0)), "workspace untouched"
+
+
 # fewer query blocks than compute units, the shapes the split is for: 8 query heads on one KV head,
 # a 2048-row chunk after 30720 cached keys (64 blocks); 8 heads on 2 KV heads, 512 rows after 65024
 # keys at D = 64 (16 blocks, each cut into 16 parts)

@@ -79,6 +79,14 @@ CONFIGS: dict[str, dict] = {
     # query blocks of 128 rows select 512-key blocks, about a quarter of the causal blocks.
     "long_ctx_32k_sel": dict(B=1, Hq=32, Hkv=8, D=128, L=2048, S=32768, causal_offset=30720, window=0,
                              amp=1.0, key_padding=None, block_sel=dict(block_q=128, block_k=512, density=0.25)),
+    # The long-context chunk on one GPU's share of a model with 64 query and 8 KV heads split over
+    # 8 GPUs by KV head: one KV head and its 8 query heads, 64 query blocks of 256 rows -- fewer than
+    # the 256 compute units. Once through the one-workgroup-per-block entry point and once through
+    # the key split with a caller workspace.
+    "few_heads_32k": dict(B=1, Hq=8, Hkv=1, D=128, L=2048, S=32768, causal_offset=30720, window=0,
+                          amp=1.0, key_padding=None),
+    "few_heads_32k_split": dict(B=1, Hq=8, Hkv=1, D=128, L=2048, S=32768, causal_offset=30720, window=0,
+                                amp=1.0, key_padding=None, entry="split"),
 }
 
 
