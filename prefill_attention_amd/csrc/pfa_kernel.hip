@@ -409,7 +409,9 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
   // ---- per-wave row state ----
   // the wave's first row, made scalar explicitly (the compiler cannot see that tid >> 6 is wave-
   // uniform): every per-wave quantity derived from it, such as the tile views, then lives in SGPRs
-  const int qw0 = q0 + __builtin_amdgcn_readfirstlane(wave) * kWaveRows;
+  // (not with a block bitmap: its per-wave bitmap state then overflowed the scalar registers, and
+  // their spills into vector registers spilled those in turn)
+  const int qw0 = q0 + (SEL ? wave : __builtin_amdgcn_readfirstlane(wave)) * kWaveRows;
   const bool wave_active = qw0 < L;
   const int ii_last = wave_active ? ((L - 1 - qw0) < 31 ? (L - 1 - qw0) : 31) : 0;
 
