@@ -56,7 +56,8 @@ long long split_part_bytes(int d);
 
 // Whether launch_prefill runs the key split for this call: a workspace is given, the layout is the
 // dense one without bias, block bitmap or rotating cache, and the call has at most 3/4 as many
-// query blocks as the split has workgroups (with more, one workgroup per block is faster).
+// query blocks as the split has workgroups (with more, one workgroup per block is faster; the
+// workspace size rule in pfa_api.cpp uses the same bound).
 bool split_applies(const Launch& p);
 
 // Query rows handled by one workgroup of the prefill kernel.
