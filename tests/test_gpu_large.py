@@ -1,5 +1,6 @@
 """Keys beyond 4 GiB per KV head: 64-bit addressing of K and V in the prefill (dense and packed
-layouts) and decode kernels, checked through a property that holds at any size.
+layouts, one workgroup per block and the key split) and decode kernels, checked through a property
+that holds at any size.
 
 With K = 0 every visible score is 0, so the softmax is uniform over the visible keys; with V = 1 for
 keys at or past 2^24 and 0 before, every output element of row i is the fraction of its visible keys
@@ -74,5 +75,17 @@ def test_decode_keys_past_4gib(kv):
     q = torch.randn(1, 1, L, D, device=DEV).to(torch.bfloat16)
     ws = torch.empty(pfa.decode_workspace_bytes(1, 1, 1, L, S, D), dtype=torch.uint8, device=DEV)
     out = pfa.prefill_attn_gqa_decode(q, k, v, workspace=ws)
+    torch.cuda.synchronize()
+    check(out, L)
+
+
+def test_prefill_key_split_keys_past_4gib(kv):
+    # one query block of one head: the key split cuts its 327,680 key tiles into 256 parts, most of
+    # them past byte 4 GiB, whose partial counts the last part merges
+    k, v = kv
+    L = 32
+    q = torch.randn(1, 1, L, D, device=DEV).to(torch.bfloat16)
+    ws = torch.zeros(pfa.prefill_workspace_bytes(1, 1, 1, L, S, D), dtype=torch.uint8, device=DEV)
+    out = pfa.prefill_attn_gqa(q, k, v, workspace=ws)
     torch.cuda.synchronize()
     check(out, L)
