@@ -343,15 +343,28 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
   // Items are numbered with the KV head slowest, so that (when the hardware deals workgroups to
   // the 8 XCDs round-robin and blockIdx is remapped accordingly) every XCD holds whole KV heads of
   // every batch element: the workgroups that share a K/V tile share an L2, and sequences of
-  // different lengths spread over all XCDs. Rank 0 is each sequence's heaviest causal block.
+  // different lengths spread over all XCDs. With the causal term the rank comes next (rank 0 is
+  // each sequence's heaviest block, so the heaviest blocks start first); without it every block of
+  // a sequence has the same work, and the batch element comes next instead, so that the
+  // workgroups running together on an XCD share one sequence's K / V (8 sequences of 4096 keys:
+  // 1414 -> 1343 us per launch).
   int item = pc.item;
+  const bool causal = p.causal != 0;
   const int g = item % p.group;
   item /= p.group;
-  const int b = item % p.batch;
-  item /= p.batch;
-  const int qrank = item % p.n_qblk;
-  const int hk = item / p.n_qblk;
-  const bool causal = p.causal != 0;
+  int b, qrank;
+  if (causal) {
+    b = item % p.batch;
+    item /= p.batch;
+    qrank = item % p.n_qblk;
+    item /= p.n_qblk;
+  } else {
+    qrank = item % p.n_qblk;
+    item /= p.n_qblk;
+    b = item % p.batch;
+    item /= p.batch;
+  }
+  const int hk = item;
   const int h = hk * p.group + g;
   // Rows and keys of this workgroup's sequence, their base elements and strides. Dense layout:
   // [B, H, L|S, D] (row stride D). Packed layout: [total, H, D] (row stride H * D), with the
@@ -1062,8 +1075,10 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
 }
 
 // The key split's walk over its linear (item, key tile) space: items in the order of the per-item
-// grid (KV head slowest, then query-block rank, batch element, head in group), each with the tiles
-// of its query block; the tile count depends on the rank only. Workgroup v of Pe takes tiles
+// grid (KV head slowest, then query-block rank, batch element, head in group; without the causal
+// term the item decodes batch element before rank, which changes nothing here since every rank
+// then has the same tiles), each with the tiles of its query block; the tile count depends on the
+// rank only. Workgroup v of Pe takes tiles
 // [T v / Pe, T (v + 1) / Pe). One thread keeps the walk in LDS and advances it between pieces, so
 // nothing of it is held in registers across a piece.
 struct SplitWalk {
