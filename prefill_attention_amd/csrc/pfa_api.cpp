@@ -314,7 +314,7 @@ namespace pfa {
 
 DecodePlan decode_plan(int B, int Hq, int Hkv, int L, int S, int D) {
   // one round of single-wave workgroups (five fit a compute unit's LDS, 256 units), at least
-  // four 32-key tiles per split; with at most 32 rows per KV head (the register-K kernel, whose
+  // four 32-key tiles per split; with one 32-row group per KV head (the register-K kernel, whose
   // waves stream the keys fastest) at least twelve, which halves the partials the merge reads and
   // still leaves about 700 workgroups for one-token decode on a 32K cache (15 % faster per call
   // than four; the 64-row kernel needs the smaller splits to fill the chip); with two 32-row groups

@@ -403,8 +403,8 @@ __global__ __launch_bounds__(64, (RB == 1 ? 2 : 1)) void pfa_decode_split_kernel
   }
 }
 
-// Decode-split kernel for at most 32 rows per KV head and no key mask (one-token decode and short
-// chunks of small groups): K goes from memory straight into the registers of the GEMM1 operand
+// Decode-split kernel for 32-row groups (up to 64 rows per KV head, as one or two groups) and no
+// key mask (one-token decode and short chunks of small groups): K goes from memory straight into the registers of the GEMM1 operand
 // (lane l: key l % 32, 16 bytes of dimensions per MFMA step, read by buffer loads whose descriptor
 // ends at the last key), only V is staged in LDS (three 32-key stages, for the transpose reads),
 // and while tile t is used tiles t+1 and t+2 are in flight: twice the bytes in flight per
