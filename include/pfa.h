@@ -207,9 +207,11 @@ int prefill_attn_gqa_ws(const void* Q, const void* K, const void* V,
                         const pfa_options* opts);
 
 /* Workspace bytes prefill_attn_gqa_ws needs for this shape (a pure function of the arguments),
- * or -1 if the shape is invalid for it: about 69 MB at D = 128 (35 MB at D = 64) of FP32 partial
- * slots plus 4 bytes per query block when the call can take the split (at most 192 query blocks),
- * else 16 (the workspace is then not touched). */
+ * or -1 if the shape is invalid for it: 1 KiB of counters (one per query block) followed by about
+ * 69 MB at D = 128 (35 MB at D = 64) of FP32 partial slots when the call can take the split (at
+ * most 192 query blocks), else 16 (the workspace is then not touched). The counters come first at
+ * a fixed place, so one zero-filled workspace serves calls of any shape and head size it is large
+ * enough for. */
 int64_t pfa_prefill_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D);
 
 /*

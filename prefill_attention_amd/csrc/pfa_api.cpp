@@ -80,15 +80,15 @@ int check_sinks(const pfa_options* opts, int Hq, Range out) {
 
 extern "C" {
 
-// Workspace of the key-split prefill for this shape: the FP32 partial slots, then one counter per
-// item (query block of a query head and batch element), rounded to 16 bytes. A shape with more
-// items than the split takes (pfa::split_applies) runs one workgroup per item and touches no
+// Workspace of the key-split prefill for this shape: the counter region (one counter per item,
+// i.e. query block of a query head and batch element), then the FP32 partial slots. A shape with
+// more items than the split takes (pfa::split_applies) runs one workgroup per item and touches no
 // workspace: 16 bytes then, so that one valid, aligned buffer still satisfies the call.
 static long long prefill_workspace_bytes(int B, int Hq, int L, int D) {
   const long long items = static_cast<long long>(B) * Hq * ((static_cast<long long>(L) + pfa::rows_per_block(D) - 1) /
                                                             pfa::rows_per_block(D));
   if (items * 4 > 3LL * pfa::kSplitWorkgroups) return 16;
-  return pfa::split_part_bytes(D) + (items * 4 + 15) / 16 * 16;
+  return pfa::kSplitCounterBytes + pfa::split_part_bytes(D);
 }
 
 // prefill_attn_gqa_opt (workspace == nullptr, use_ws false) or prefill_attn_gqa_ws.

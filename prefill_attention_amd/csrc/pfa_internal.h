@@ -43,13 +43,19 @@ struct Launch {
   const uint8_t* sel = nullptr;
   int sel_bq = 0, sel_bk = 0;
   long long sel_sb = 0, sel_sh = 0, sel_sq = 0;
-  // Key-split workspace (null = one workgroup per item): split_part_bytes(d) of FP32 partials, then
-  // one zero counter per item (zero on entry, left zero on return).
+  // Key-split workspace (null = one workgroup per item): kSplitCounterBytes of counters, one per
+  // item (zero on entry, left zero on return), then split_part_bytes(d) of FP32 partials. The
+  // counters sit at a fixed place so that no call's partials, whatever its head size, land on them.
   void* workspace = nullptr;
 };
 
 // Workgroups of a key-split launch (one per compute unit of an MI355X).
 constexpr int kSplitWorkgroups = 256;
+
+// Counter region at the start of a key-split workspace: one 4-byte counter per item, and the split
+// is taken with at most 3/4 * kSplitWorkgroups items.
+constexpr long long kSplitCounterBytes = 1024;
+static_assert(kSplitCounterBytes >= 4LL * (3 * kSplitWorkgroups / 4), "split counters");
 
 // Bytes of FP32 partial slots a key-split launch uses (two per workgroup), before the counters.
 long long split_part_bytes(int d);

@@ -1272,8 +1272,8 @@ int launch_variant(const pfa::Launch& L) {
   const void* fn;
   if (split) {
     // key split over a fixed set of workgroups (one per compute unit of an MI355X)
-    p.ws_part = static_cast<float*>(L.workspace);
-    p.ws_cnt = reinterpret_cast<unsigned*>(static_cast<char*>(L.workspace) + pfa::split_part_bytes(L.d));
+    p.ws_cnt = static_cast<unsigned*>(L.workspace);
+    p.ws_part = reinterpret_cast<float*>(static_cast<char*>(L.workspace) + pfa::kSplitCounterBytes);
     if (L.key_mask)
       fn = sc ? reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeKeyMask | kModeSoftcap, true>)
               : reinterpret_cast<const void*>(&pfa_prefill_kernel<D, kModeKeyMask, true>);

@@ -234,11 +234,12 @@ def test_prefill_ws_invalid_arguments_rejected(lib, kw, code):
 
 
 def test_prefill_workspace_bytes_function(lib):
-    # FP32 partial slots of the 256 split workgroups (two each) plus one 4-byte counter per item
+    # FP32 partial slots of the 256 split workgroups (two each) and one 4-byte counter per item
+    # a 1 KiB counter region first, then the partial slots
     slots128 = 2 * 256 * 8 * 64 * (16 * 4 + 2) * 4
-    assert pfa.prefill_workspace_bytes(1, 8, 1, 2048, 32768, 128) == slots128 + 8 * 8 * 4
-    assert pfa.prefill_workspace_bytes(1, 4, 2, 33, 47, 64) == 2 * 256 * 8 * 64 * (16 * 2 + 2) * 4 + 16
-    assert pfa.prefill_workspace_bytes(1, 48, 8, 1024, 4096, 128) == slots128 + 192 * 4  # 192 blocks: split
+    assert pfa.prefill_workspace_bytes(1, 8, 1, 2048, 32768, 128) == 1024 + slots128
+    assert pfa.prefill_workspace_bytes(1, 4, 2, 33, 47, 64) == 1024 + 2 * 256 * 8 * 64 * (16 * 2 + 2) * 4
+    assert pfa.prefill_workspace_bytes(1, 48, 8, 1024, 4096, 128) == 1024 + slots128  # 192 blocks: split
     # more than 192 query blocks: one workgroup per block, no workspace used (a 16-byte token)
     assert pfa.prefill_workspace_bytes(1, 56, 8, 2048, 8192, 128) == 16
     assert pfa.prefill_workspace_bytes(1, 193, 1, 256, 4096, 64) == 16

@@ -47,11 +47,9 @@ def workspace_for(q_shape, k_shape):
     return torch.zeros(need, dtype=torch.uint8, device=DEV)
 
 
-def counters_zero(ws, shape):
-    """The per-query-block counters of a call on q of this shape, after its FP32 partial slots."""
-    B, Hq, L, D = shape
-    part = 2 * 256 * 8 * 64 * (16 * (D // 32) + 2) * 4
-    return bool(torch.all(ws[part:part + 4 * B * Hq * ((L + 255) // 256)] == 0))
+def counters_zero(ws, shape=None):
+    """The per-query-block counters at the start of the workspace (1 KiB) are all zero."""
+    return bool(torch.all(ws[:1024] == 0))
 
 
 def run(x, ws, no_skip=False, softcap=0.0, sinks=None):
@@ -214,3 +212,23 @@ def test_split_close_to_per_item_grid():
     b = pfa.prefill_attn_gqa(q, k, v, scale=float(x["scale"]), causal_offset=x["causal_offset"])
     torch.cuda.synchronize()
     check_close(a.double().cpu().numpy(), b.double().cpu().numpy(), "split vs per-item grid")
+
+
+def test_workspace_reused_across_head_sizes():
+    """One zero-filled workspace through calls of both head sizes: a D = 128 call whose parts fill
+    the whole partial region, then a D = 64 call (its partial slots sit elsewhere), then D = 128
+    again. The counters live at a fixed place, so each call still merges exactly its own parts: each
+    result matches the per-item call within the tolerance, and the repeated call is bit-identical."""
+    big = make_inputs(FEW_BLOCKS["h8_kv1_32k"], seed=21)
+    small = make_inputs(FEW_BLOCKS["h8_kv2_64k_d64"], seed=22)
+    need = max(pfa.prefill_workspace_bytes(x["B"], x["Hq"], x["Hkv"], x["L"], x["S"], x["D"]) for x in (big, small))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    print("[split] workspace reused across head sizes", flush=True)
+    a1 = run(big, ws)
+    s1 = run(small, ws)
+    a2 = run(big, ws)
+    assert counters_zero(ws)
+    assert torch.equal(a1.view(torch.int16), a2.view(torch.int16))
+    for got, x, what in ((s1, small, "D=64 after D=128"), (a2, big, "D=128 after D=64")):
+        ref = run(x, None)
+        check_close(got.double().cpu().numpy(), ref.double().cpu().numpy(), what)
