@@ -165,8 +165,12 @@ def prefill_attn_gqa(q, k, v, *, scale: float | None = None, causal: bool = True
     scaled scores before the masks. sinks: optional float32 [Hq] attention-sink logits (one extra
     softmax term per head, with no value). block_sel: optional uint8/bool block bitmap broadcastable
     to [B, Hq, ceil(L/block_q), ceil(S/block_k)] (last dimension contiguous); key j is visible to
-    row i only where block_sel[b, h, i // block_q, j // block_k] is nonzero. Returns `out`
-    (allocated if None), bf16 [B,Hq,L,D].
+    row i only where block_sel[b, h, i // block_q, j // block_k] is nonzero. workspace: optional
+    zero-filled contiguous uint8 tensor on q's device of at least prefill_workspace_bytes(...)
+    bytes; with it a call with at most 192 query blocks of 256 rows splits its keys over the whole
+    chip (prefill_attn_gqa_ws), others run as without it. Every call leaves it ready for the next
+    (of any shape it is large enough for); calls sharing it must be ordered on one stream. Returns
+    `out` (allocated if None), bf16 [B,Hq,L,D].
     """
     import torch
 
