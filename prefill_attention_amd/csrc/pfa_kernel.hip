@@ -1059,9 +1059,13 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
   // (overflow to +inf gives O = 0, the limit; a -inf sink adds 0)
   if (p.sinks != nullptr && lt > 0.0f) lt += __builtin_amdgcn_exp2f(__builtin_fmaf(p.sinks[h], kLog2e, -mref));
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  const int row = qw0 + l32;
-  if (row >= L) return;
-  uint16_t* orow = p.o + q_base + (long long)row * q_stride;
+  // The lane holds 8-byte pieces of its row; stored as they are, every store instruction would
+  // touch 32 rows with 16 bytes each. They go through the wave's own 32 rows of LDS instead (the
+  // stages are free: the loop's last barrier follows every wave's last read of them, and no fetch
+  // is in flight), 16-byte chunks XOR-swizzled by row, and leave as whole rows: 16-byte stores,
+  // consecutive lanes on consecutive chunks.
+  constexpr int kChunks = G::kRowBytes / 16;  // 16-byte chunks per row
+  lds_char* obuf = (lds_char*)lds_raw + wave * (kWaveRows * G::kRowBytes);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -1069,8 +1073,19 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
       bf16x4 ov;
 #pragma unroll
       for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(acc[db][4 * j + i] * inv);
-      *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * j + 4 * hh) = ov;
+      const int c = (4 * db + j) ^ (l32 & (kChunks - 1));
+      *(__attribute__((address_space(3))) bf16x4*)(obuf + l32 * G::kRowBytes + 16 * c + 8 * hh) = ov;
     }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the writes of the other lanes are in LDS
+  constexpr int kRowsPerStore = 64 / kChunks;
+  const int cl = lane % kChunks;
+#pragma unroll
+  for (int i = 0; i < kWaveRows / kRowsPerStore; ++i) {
+    const int r = i * kRowsPerStore + lane / kChunks;
+    const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(obuf + r * G::kRowBytes +
+                                                                         16 * (cl ^ (r & (kChunks - 1))));
+    if (qw0 + r < L) *reinterpret_cast<u32x4*>(p.o + q_base + (long long)(qw0 + r) * q_stride + 8 * cl) = v;
   }
 }
 
