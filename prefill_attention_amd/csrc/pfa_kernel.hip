@@ -551,22 +551,29 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
     const int sw = group_a ? G::swz_k(row) : G::swz_v(row);
     dma_off[j] = (unsigned)(row * 2 * kv_stride + 16 * (pch ^ sw));
   }
-  // wave-uniform values, made scalar explicitly (the compiler cannot see that tid >> 6 is)
-  const uint16_t* dma_src = group_a ? kg : vg;
+  // wave-uniform values, made scalar explicitly (the compiler cannot see that tid >> 6 is), so
+  // that a fetch's address arithmetic is scalar only: with the source pointer in vector registers
+  // it went through a vector add and two readfirstlanes, and each fetch cost a few hundred cycles
+  // after the MFMA phase
   const int dma_lds = __builtin_amdgcn_readfirstlane((group_a ? 0 : G::kTileBytes) + w4 * G::kDmaPerWave * 1024);
+  unsigned long long dma_src;
+  {
+    // readfirstlane returns int: go through unsigned so the low word is not sign-extended
+    const uintptr_t a = reinterpret_cast<uintptr_t>(group_a ? kg : vg);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32));
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a);
+    dma_src = ((unsigned long long)hi << 32) | lo;
+  }
+  const int tile_bytes = kBN * 2 * kv_stride;  // < 2^31: kv_stride < 2^24
   uint8_t mreg = 0;
   // this wave's share of matrix (K for waves 0-3, V for 4-7) of tile kt into stage st
   auto issue = [&](int kt, int st) __attribute__((always_inline)) {
-    const long long key0 = (long long)kt * kBN;
-    const long long rows = (long long)S - key0;
+    const int key0 = kt * kBN;  // kt * 64 <= S + 63 < 2^31
+    const int rows = S - key0;
     constexpr bool ring = RING;  // rotating cache (p.ring slots)
     // ring cache: the descriptor covers the whole ring
-    const int nrec = ring ? p.ring * G::kRowBytes : (rows < kBN ? (int)rows : kBN) * 2 * kv_stride;
-    const uintptr_t base = reinterpret_cast<uintptr_t>(ring ? dma_src : dma_src + key0 * kv_stride);
-    // readfirstlane returns int: go through unsigned so the low word is not sign-extended
-    const unsigned base_hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(base >> 32));
-    const unsigned base_lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)base);
-    const uintptr_t base_u = ((uintptr_t)base_hi << 32) | (uintptr_t)base_lo;
+    const int nrec = ring ? p.ring * G::kRowBytes : (rows < kBN ? rows : kBN) * 2 * kv_stride;
+    const uintptr_t base_u = ring ? dma_src : dma_src + (unsigned long long)(unsigned)kt * (unsigned)tile_bytes;
     lds_char* dst = (lds_char*)lds_raw + st * G::kStageBytes + dma_lds;
     if constexpr (!ring) {
       dma_rows<G::kDmaPerWave>(reinterpret_cast<const void*>(base_u), __builtin_amdgcn_readfirstlane(nrec),
