@@ -11,8 +11,11 @@ D=128 chunks that the throughput target is quoted on: 2048 new rows on an 8192-k
 (Hq=56, Hkv=8) and 2048 new rows on a 32768-key context (Hq=32, Hkv=8). Prints one JSON line.
 
 value = useful TFLOP/s = 4 * D * (visible query-key pairs) / time, whole job.
+Defaults: at least 50 timed steps and 5 warm-up steps, and at least 0.1 s of each (short launches run
+more steps); explicit --steps / --warmup are taken as given.
 roofline: the prefill kernel against the bf16 dense MFMA peak, with its average launch duration
-taken from HIP events recorded on the launch stream around every launch of the timed region.
+taken from HIP events recorded on the launch stream around every launch of a second timed pass
+(launches under a millisecond in runs of back-to-back launches between two events).
 cpu_baseline: the fp64 CPU oracle, timed on a bounded sample of the same workload.
 --cold-mib N: every launch reads a different copy of Q, K, V and the key mask (and writes a different
 O), cycling through enough copies to exceed N MiB, so that no launch finds its operands in the L2 or
@@ -28,6 +31,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -306,8 +310,11 @@ def varlen_cpu_baseline(name: str, workers: int, budget_s: float = 20.0) -> dict
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # default K / W: at least 50 timed steps and 5 warm-up steps, and at least 0.1 s of timed work and
+    # of warm-up (a short launch, such as a decode call of 25 us, then runs a few thousand steps, so
+    # the clock has settled and the timed region is not a few milliseconds long)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="causal_8k_32k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -430,17 +437,29 @@ def main() -> int:
         per_cfg.append(dict(name=name, flops=flops, rows=c["B"] * c["L"], bytes=algorithmic_bytes(c)))
     torch.cuda.synchronize()
 
-    def step(events=None):
-        for idx, (name, launch) in enumerate(calls):
-            if events is not None:
-                events[idx][0].record()
+    def step():
+        for name, launch in calls:
             launch()
-            if events is not None:
-                events[idx][1].record()
 
-    for _ in range(args.warmup):
+    # warm-up: the given number of steps, or (default) at least 5 steps and 0.1 s; the default step
+    # count then comes from the warm-up's second half (past the first, slower calls)
+    t0 = time.perf_counter()
+    done, t_half, n_half = 0, None, 0
+    while (done < args.warmup) if args.warmup is not None else (done < 5 or time.perf_counter() - t0 < 0.1):
         step()
+        done += 1
+        if done % 8 == 0:
+            torch.cuda.synchronize()
+            if t_half is None and time.perf_counter() - t0 >= 0.05:
+                t_half, n_half = time.perf_counter(), done
     torch.cuda.synchronize()
+    if t_half is not None and done > n_half:
+        est = (time.perf_counter() - t_half) / (done - n_half)
+    else:
+        est = (time.perf_counter() - t0) / max(done, 1)
+    args.warmup = done
+    if args.steps is None:
+        args.steps = max(50, min(5000, math.ceil(0.1 / max(est, 1e-6)))) if done > 0 else 50
 
     # whole-step timing
     t0 = time.perf_counter()
@@ -449,14 +468,22 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per-launch durations (HIP events on the launch stream = torch's current stream)
+    # per-launch durations (HIP events on the launch stream = torch's current stream). A launch
+    # shorter than a millisecond is timed in runs of `rep` back-to-back launches between two events,
+    # so that the event records between launches do not add their dispatch gaps to it.
+    rep = max(1, math.ceil(1e-3 / (wall / args.steps)))
+    rounds = max(5, math.ceil(args.steps / rep))
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in calls] for _ in range(args.steps)]
+           for _ in calls] for _ in range(rounds)]
     torch.cuda.synchronize()
-    for s in range(args.steps):
-        step(ev[s])
+    for s in range(rounds):
+        for idx, (name, launch) in enumerate(calls):
+            ev[s][idx][0].record()
+            for _ in range(rep):
+                launch()
+            ev[s][idx][1].record()
     torch.cuda.synchronize()
-    per_launch_ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)] for i in range(len(calls))]
+    per_launch_ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) / rep for s in range(rounds)] for i in range(len(calls))]
     mean_ms = [float(np.mean(v)) for v in per_launch_ms]
 
     ms_per_step = wall * 1e3 / args.steps
