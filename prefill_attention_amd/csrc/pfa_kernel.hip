@@ -1046,14 +1046,20 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
       for (int v = 0; v < 16; ++v) acc[db][v] = 0.0f;
     for (int k = 0; k < pc.n_parts; ++k) {
       const unsigned src = part_base(part_slot(pc.v_first + k, k == 0));
-      const float mk = part_load(rs, src + (16 * DB) * 256);
+      // all of a part's loads are issued before the first is used (the scheduling barrier keeps
+      // the compiler from waiting for each load before issuing the next, which it did in the
+      // key-mask instantiations and which made a 16-part merge hundreds of microseconds long)
+      float x[16 * DB + 2];
+#pragma unroll
+      for (int i = 0; i < 16 * DB + 2; ++i) x[i] = part_load(rs, src + i * 256);
+      __builtin_amdgcn_sched_barrier(0);
+      const float mk = x[16 * DB];
       const float w = (mk == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mk - mm);
-      l_run = __builtin_fmaf(part_load(rs, src + (16 * DB + 1) * 256), w, l_run);
+      l_run = __builtin_fmaf(x[16 * DB + 1], w, l_run);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          acc[db][v] = __builtin_fmaf(part_load(rs, src + (16 * db + v) * 256), w, acc[db][v]);
+        for (int v = 0; v < 16; ++v) acc[db][v] = __builtin_fmaf(x[16 * db + v], w, acc[db][v]);
     }
     mref = mm;
     if (tid == 0) __hip_atomic_store(&p.ws_cnt[pc.item], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
