@@ -69,6 +69,9 @@ bool split_applies(const Launch& p);
 // Query rows handled by one workgroup of the prefill kernel.
 int rows_per_block(int d);
 
+// Query heads of one KV group that share a workgroup of the per-item launch (1, 2 or 4).
+int heads_per_block(const Launch& p);
+
 // Number of workgroups the launch will use (64-bit; the caller checks it fits the grid).
 long long grid_blocks(const Launch& p);
 

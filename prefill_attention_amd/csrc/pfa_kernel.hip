@@ -134,6 +134,12 @@ struct Params {
   unsigned* ws_cnt;
   int batch;
   int n_qblk;
+  // Query heads of one KV group that share a workgroup (1, 2 or 4; 1 with a bias, a bitmap or the
+  // key split): wave w takes head (w mod hpw) of the item's head set and rows 32 (w / hpw) of the
+  // item's block of 256 / hpw rows. Every head of the set reads the same K / V tiles, and the
+  // block's key range (causal and window edges) narrows with its height.
+  int hpw;
+  int n_hset;  // group / hpw head sets per KV head
   int n_wg;
   int xcd_remap;
 };
@@ -350,8 +356,11 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
   // 1414 -> 1343 us per launch).
   int item = pc.item;
   const bool causal = p.causal != 0;
-  const int g = item % p.group;
-  item /= p.group;
+  // a bias or a bitmap is laid out per head and row block: one head per workgroup there
+  const int hpw = (BIAS || SEL) ? 1 : p.hpw;
+  const int bm = kBM / hpw;  // query rows of the item
+  const int hset = item % p.n_hset;
+  item /= p.n_hset;
   int b, qrank;
   if (causal) {
     b = item % p.batch;
@@ -365,7 +374,12 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
     item /= p.batch;
   }
   const int hk = item;
-  const int h = hk * p.group + g;
+  // the wave's head and row chunk, made scalar explicitly (the compiler cannot see that tid >> 6 is
+  // wave-uniform): every per-wave quantity derived from them, such as the tile views, then lives in
+  // SGPRs (not with a block bitmap: its per-wave bitmap state then overflowed the scalar registers,
+  // and their spills into vector registers spilled those in turn)
+  const int wv = SEL ? wave : __builtin_amdgcn_readfirstlane(wave);
+  const int h = hk * p.group + hset * hpw + wv % hpw;
   // Rows and keys of this workgroup's sequence, their base elements and strides. Dense layout:
   // [B, H, L|S, D] (row stride D). Packed layout: [total, H, D] (row stride H * D), with the
   // sequence bounds clamped to the packed extents so that malformed prefix sums stay in bounds.
@@ -394,11 +408,11 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
     kv_stride = p.hkv * D;
   }
   const int W = p.window;
-  const int nb = (L + kBM - 1) / kBM;  // query blocks of this sequence
+  const int nb = (L + bm - 1) / bm;  // query blocks of this sequence
   if (qrank >= nb) return;  // past the end of a shorter sequence: the whole workgroup leaves
   const int qblk = causal ? (nb - 1 - qrank) : qrank;
-  const int q0 = qblk * kBM;
-  const int q1 = (q0 + kBM) < L ? (q0 + kBM) : L;
+  const int q0 = qblk * bm;
+  const int q1 = (q0 + bm) < L ? (q0 + bm) : L;
 
   const uint16_t* kg = p.k + kv_base;
   const uint16_t* vg = p.v + kv_base;
@@ -420,11 +434,7 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
   }
 
   // ---- per-wave row state ----
-  // the wave's first row, made scalar explicitly (the compiler cannot see that tid >> 6 is wave-
-  // uniform): every per-wave quantity derived from it, such as the tile views, then lives in SGPRs
-  // (not with a block bitmap: its per-wave bitmap state then overflowed the scalar registers, and
-  // their spills into vector registers spilled those in turn)
-  const int qw0 = q0 + (SEL ? wave : __builtin_amdgcn_readfirstlane(wave)) * kWaveRows;
+  const int qw0 = q0 + (wv / hpw) * kWaveRows;  // the wave's first row
   const bool wave_active = qw0 < L;
   const int ii_last = wave_active ? ((L - 1 - qw0) < 31 ? (L - 1 - qw0) : 31) : 0;
 
@@ -1276,8 +1286,11 @@ int launch_variant(const pfa::Launch& L) {
   p.ws_cnt = nullptr;
   p.ring = L.ring;
   p.batch = L.batch;
-  p.n_qblk = (L.lq + kBM - 1) / kBM;
-  const long long n = (long long)L.batch * L.hq * p.n_qblk;
+  const bool split = pfa::split_applies(L);
+  p.hpw = split ? 1 : pfa::heads_per_block(L);
+  p.n_hset = L.group / p.hpw;
+  p.n_qblk = (L.lq + kBM / p.hpw - 1) / (kBM / p.hpw);
+  const long long n = (long long)L.batch * (L.hq / p.hpw) * p.n_qblk;
   p.n_wg = (int)n;
   p.xcd_remap = (n % kXcds) == 0 ? 1 : 0;
   void* args[] = {&p};
@@ -1296,7 +1309,6 @@ int launch_variant(const pfa::Launch& L) {
   p.sel_sb = L.sel_sb;
   p.sel_sh = L.sel_sh;
   p.sel_sq = L.sel_sq;
-  const bool split = pfa::split_applies(L);
   const void* fn;
   if (split) {
     // key split over a fixed set of workgroups (one per compute unit of an MI355X)
@@ -1373,19 +1385,32 @@ int launch_ring_append(const void* k_new, const void* v_new, void* k_ring, void*
 
 int rows_per_block(int) { return kBM; }
 
+// The band of a windowed call narrows with the block's height: 256 rows of one head see W + 255
+// keys, 64 rows of each of four heads W + 63, for the same work. Causal and bidirectional calls keep
+// one head per workgroup (their blocks' heights change nothing but the order of the work).
+int heads_per_block(const Launch& p) {
+  if (p.bias != nullptr || p.sel != nullptr || p.window <= 0) return 1;
+  if (p.group % 4 == 0) return 4;
+  if (p.group % 2 == 0) return 2;
+  return 1;
+}
+
 long long split_part_bytes(int d) {
   const long long floats = d == 128 ? Slot<128>::kFloats : Slot<64>::kFloats;
   return 2LL * kSplitWorkgroups * floats * 4;
 }
 
 bool split_applies(const Launch& p) {
+  const long long items = (long long)p.batch * p.hq * ((p.lq + kBM - 1) / kBM);  // one head per item
   return p.workspace != nullptr && p.cu_q == nullptr && p.ring == 0 && p.bias == nullptr && p.sel == nullptr &&
-         grid_blocks(p) * 4 <= 3LL * kSplitWorkgroups;
+         items * 4 <= 3LL * kSplitWorkgroups;
 }
 
 long long grid_blocks(const Launch& p) {
-  const long long bm = rows_per_block(p.d);
-  return (long long)p.batch * p.hq * ((p.lq + bm - 1) / bm);
+  if (split_applies(p)) return kSplitWorkgroups;
+  const long long hpw = heads_per_block(p);
+  const long long bm = kBM / hpw;
+  return (long long)p.batch * (p.hq / hpw) * ((p.lq + bm - 1) / bm);
 }
 
 int launch_prefill(const Launch& p) {
