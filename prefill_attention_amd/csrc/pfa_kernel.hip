@@ -743,18 +743,24 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
       }
     }
   };
-  // With a block bitmap a wave often has no keys in the tile (its query block did not select
-  // it) while the workgroup visits it for the other waves: then its GEMM1 (scores never used)
-  // and its GEMM2 of a tile without keys (P = 0, adding exact zeros) are left out.
-  auto mfma_phase = [&](int st1, int st2, bool live1, bool live2) __attribute__((always_inline)) {
+  // g1 / g2 (constants): whether the iteration has a current tile (GEMM1) and a previous one
+  // (GEMM2); the first iteration of a piece has no previous tile (P would be zero) and the last no
+  // current one (its scores would never be used), so they leave that GEMM out. With a block bitmap
+  // a wave often has no keys in the tile (its query block did not select it) while the workgroup
+  // visits it for the other waves: then its GEMM1 (scores never used) and its GEMM2 of a tile
+  // without keys (P = 0, adding exact zeros) are left out as well.
+  auto mfma_phase = [&](int st1, int st2, bool live1, bool live2, auto g1, auto g2) __attribute__((always_inline)) {
     using T = std::true_type;
     using F = std::false_type;
+    constexpr bool G1 = decltype(g1)::value;
+    constexpr bool G2 = decltype(g2)::value;
     if constexpr (SEL) {
-      if (live1 && live2) mfma_run(st1, st2, T{}, T{});
-      else if (live1) mfma_run(st1, st2, T{}, F{});
-      else if (live2) mfma_run(st1, st2, F{}, T{});
+      const bool l1 = G1 && live1, l2 = G2 && live2;
+      if (l1 && l2) mfma_run(st1, st2, T{}, T{});
+      else if (l1) mfma_run(st1, st2, T{}, F{});
+      else if (l2) mfma_run(st1, st2, F{}, T{});
     } else {
-      mfma_run(st1, st2, T{}, T{});
+      mfma_run(st1, st2, g1, g2);
     }
   };
 
@@ -952,58 +958,66 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
   // the loop behind a branch on a wave-uniform value, so the compiler sees each group's own tile
   // fetches only and does not make one group's LDS reads wait for the loads of the other: its
   // bias loads. Without a bias the shared loop is the faster one.)
-  auto main_loop = [&](auto group) __attribute__((always_inline)) {
+  // One iteration; g1 / g2 (constants) say whether it has a current and a previous tile: the loop
+  // runs one iteration without a previous tile, then full ones, then one without a current tile.
+  auto iteration = [&](auto group, auto g1, auto g2) __attribute__((always_inline)) {
+    constexpr bool G1 = decltype(g1)::value;
+    constexpr bool G2 = decltype(g2)::value;
     const bool GA = group;
-    bool first_iter = true;  // tile cur of the first iteration was fetched whole by the prologue
-    while (cur < kt_hi || prv < kt_hi) {
-      const int packed_nxt = next_tile(cur + 1 <= kt_hi ? cur + 1 : kt_hi);
-      const int nxt = packed_nxt >> 1;
-      const bool all_nxt = packed_nxt & 1;
-      const int st_nxt = st_cur + 1 == kStages ? 0 : st_cur + 1;
-      if (cur < kt_hi) {
-        tv_cur = view_of(cur, all_cur);
-      } else {
-        tv_cur.live = false;
+    const int packed_nxt = next_tile(cur + 1 <= kt_hi ? cur + 1 : kt_hi);
+    const int nxt = packed_nxt >> 1;
+    const bool all_nxt = packed_nxt & 1;
+    const int st_nxt = st_cur + 1 == kStages ? 0 : st_cur + 1;
+    if constexpr (G1) {
+      tv_cur = view_of(cur, all_cur);
+    } else {
+      tv_cur.live = false;
+    }
+    // first half
+    if (GA) {
+      if constexpr (G1) bias_fetch(cur);  // for this iteration's softmax (second half)
+      mfma_phase(st_cur, st_prv, tv_cur.live, tv_prv.live, g1, g2);
+      if (nxt < kt_hi) issue(nxt, st_nxt);  // K of tile nxt
+    } else {
+      // With a bias, V of tile cur is fetched here rather than at the end of the previous
+      // iteration: no tile fetch is then in flight across the loop edge, so the MFMA phase's
+      // LDS reads need not wait for the bias loads issued just before it. (Tile cur of the first
+      // iteration was fetched whole by the prologue.)
+      if constexpr (BIAS && G1 && G2) issue(cur, st_cur);
+      if constexpr (G2) softmax_phase(tv_prv, st_prv);  // (first iteration: P is still zero)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // V of tile cur has landed
+    }
+    // Nothing stored to LDS in the first half is read in the second (the K in flight targets
+    // the stage nobody reads this iteration), so the middle barrier only aligns the phases.
+    __builtin_amdgcn_s_barrier();
+    // second half
+    if (GA) {
+      if constexpr (G1) softmax_phase(tv_cur, st_cur);
+      if (nxt < kt_hi) finish(st_nxt);
+      // with a bias, also wait where no fetch was issued, so that no path leaves one in flight
+      if constexpr (BIAS) __builtin_amdgcn_s_waitcnt(0x0F70);
+    } else {
+      bias_fetch(cur);  // for the next iteration's softmax (first half), whose tile is this cur
+      mfma_phase(st_cur, st_prv, tv_cur.live, tv_prv.live, g1, g2);
+      if constexpr (!BIAS) {
+        if (nxt < kt_hi) issue(nxt, st_nxt);  // V of tile nxt: first read one iteration later
       }
-      // first half
-      if (GA) {
-        bias_fetch(cur);  // for this iteration's softmax (second half)
-        mfma_phase(st_cur, st_prv, tv_cur.live, tv_prv.live);
-        if (nxt < kt_hi) issue(nxt, st_nxt);  // K of tile nxt
-      } else {
-        // With a bias, V of tile cur is fetched here rather than at the end of the previous
-        // iteration: no tile fetch is then in flight across the loop edge, so the MFMA phase's
-        // LDS reads need not wait for the bias loads issued just before it.
-        if constexpr (BIAS) {
-          if (!first_iter && cur < kt_hi) issue(cur, st_cur);
-        }
-        softmax_phase(tv_prv, st_prv);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // V of tile cur has landed
-      }
-      // Nothing stored to LDS in the first half is read in the second (the K in flight targets
-      // the stage nobody reads this iteration), so the middle barrier only aligns the phases.
-      __builtin_amdgcn_s_barrier();
-      // second half
-      if (GA) {
-        softmax_phase(tv_cur, st_cur);
-        if (nxt < kt_hi) finish(st_nxt);
-        // with a bias, also wait where no fetch was issued, so that no path leaves one in flight
-        if constexpr (BIAS) __builtin_amdgcn_s_waitcnt(0x0F70);
-      } else {
-        bias_fetch(cur);  // for the next iteration's softmax (first half), whose tile is this cur
-        mfma_phase(st_cur, st_prv, tv_cur.live, tv_prv.live);
-        if constexpr (!BIAS) {
-          if (nxt < kt_hi) issue(nxt, st_nxt);  // V of tile nxt: first read one iteration later
-        }
-      }
-      lds_barrier();
-      if constexpr (BIAS) first_iter = false;
-      prv = cur;
-      tv_prv = tv_cur;
-      st_prv = st_cur;
-      cur = nxt;
-      all_cur = all_nxt;
-      st_cur = st_nxt;
+    }
+    lds_barrier();
+    prv = cur;
+    tv_prv = tv_cur;
+    st_prv = st_cur;
+    cur = nxt;
+    all_cur = all_nxt;
+    st_cur = st_nxt;
+  };
+  auto main_loop = [&](auto group) __attribute__((always_inline)) {
+    using T = std::true_type;
+    using F = std::false_type;
+    if (cur < kt_hi) {
+      iteration(group, T{}, F{});
+      while (cur < kt_hi) iteration(group, T{}, T{});
+      iteration(group, F{}, T{});
     }
   };
   if constexpr (BIAS) {
