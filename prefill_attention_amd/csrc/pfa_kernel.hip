@@ -79,7 +79,13 @@ template <int D>
 struct Geo {
   static constexpr int kRowBytes = 2 * D;              // unpadded K / V row in LDS
   static constexpr int kTileBytes = kBN * kRowBytes;   // one K or V tile
-  static constexpr int kStageBytes = 2 * kTileBytes;   // K then V
+  static constexpr int kStageBytes = 2 * kTileBytes;   // one K and one V tile
+  // LDS: the K tiles of the stages first, then their V tiles, so that every operand read of an
+  // iteration with a known stage is one lane address plus an immediate offset below 64 KB
+  static constexpr int kVRegion = kStages * kTileBytes;
+  // part of the V region's offset held in the lane's V^T read addresses rather than in the
+  // immediate offsets (those of stage 2 would pass 64 KB at D = 128)
+  static constexpr int kVHeld = D == 128 ? 32768 : 0;
   static constexpr int kChunksPerRow = D / 8;          // 16-byte chunks per row
   static constexpr int kRowsPerDma = 1024 / kRowBytes;  // rows written by one DMA instruction
   static constexpr int kDmaPerTile = kTileBytes / 1024;
@@ -565,7 +571,7 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
   // that a fetch's address arithmetic is scalar only: with the source pointer in vector registers
   // it went through a vector add and two readfirstlanes, and each fetch cost a few hundred cycles
   // after the MFMA phase
-  const int dma_lds = __builtin_amdgcn_readfirstlane((group_a ? 0 : G::kTileBytes) + w4 * G::kDmaPerWave * 1024);
+  const int dma_lds = __builtin_amdgcn_readfirstlane((group_a ? 0 : G::kVRegion) + w4 * G::kDmaPerWave * 1024);
   unsigned long long dma_src;
   {
     // readfirstlane returns int: go through unsigned so the low word is not sign-extended
@@ -584,7 +590,7 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
     // ring cache: the descriptor covers the whole ring
     const int nrec = ring ? p.ring * G::kRowBytes : (rows < kBN ? rows : kBN) * 2 * kv_stride;
     const uintptr_t base_u = ring ? dma_src : dma_src + (unsigned long long)(unsigned)kt * (unsigned)tile_bytes;
-    lds_char* dst = (lds_char*)lds_raw + st * G::kStageBytes + dma_lds;
+    lds_char* dst = (lds_char*)lds_raw + st * G::kTileBytes + dma_lds;
     if constexpr (!ring) {
       dma_rows<G::kDmaPerWave>(reinterpret_cast<const void*>(base_u), __builtin_amdgcn_readfirstlane(nrec),
                                dst, dma_off);
@@ -612,7 +618,7 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   };
 
-  // ---- per-lane LDS read addresses (byte offsets inside a stage) ----
+  // ---- per-lane LDS read addresses (byte offsets inside a K or V tile) ----
   // K (GEMM1 A operand): row l32 (+32 kb), logical chunk 2kk+hh -> address a_k ^ (32 kk).
   int a_k;
   {
@@ -626,7 +632,15 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
     const int g16 = lane >> 4, loc = lane & 15, r4 = loc >> 2, cc = loc & 3;
     const int row = 4 * (g16 >> 1) + r4;
     const int sv = G::swz_v(row) >> 2;  // swizzle of the 64-byte column block
-    a_v = G::kTileBytes + row * G::kRowBytes + 64 * sv + 32 * (g16 & 1) + 8 * cc;
+    a_v = row * G::kRowBytes + 64 * sv + 32 * (g16 & 1) + 8 * cc;
+  }
+  // the four V^T read addresses of the lane, with kVHeld added; the empty asm hides the addition
+  // from the compiler, which would otherwise fold it back into (too large) immediate offsets
+  int a_vh[G::DB];
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db) {
+    a_vh[db] = (a_v ^ (64 * db)) + G::kVHeld;
+    asm volatile("" : "+v"(a_vh[db]));
   }
 
   // ---- per-wave view of one tile: mask thresholds, skip and mask decisions ----
@@ -689,15 +703,15 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
   auto mfma_run = [&](int st1, int st2, auto do_g1, auto do_g2) __attribute__((always_inline)) {
     constexpr bool DO1 = decltype(do_g1)::value;
     constexpr bool DO2 = decltype(do_g2)::value;
-    const lds_char* base1 = (const lds_char*)lds_raw + st1 * G::kStageBytes;
-    const lds_char* base2 = (const lds_char*)lds_raw + st2 * G::kStageBytes;
+    const lds_char* base1 = (const lds_char*)lds_raw + st1 * G::kTileBytes;
+    const lds_char* base2 = (const lds_char*)lds_raw + (G::kVRegion - G::kVHeld) + st2 * G::kTileBytes;
     auto load_g1 = [&](int j) __attribute__((always_inline)) -> bf16x8 {
       const int kb = j / KQ, kk = j % KQ;
       return *(const lds_bf16x8*)(base1 + kb * 32 * G::kRowBytes + (a_k ^ (32 * kk)));
     };
     auto load_g2 = [&](int j) __attribute__((always_inline)) -> bf16x8 {
       const int kb = j / (2 * DB), c2 = (j / DB) & 1, db = j % DB;
-      const lds_char* pr = base2 + (kb * 32 + 16 * c2) * G::kRowBytes + (a_v ^ (64 * db));
+      const lds_char* pr = base2 + (kb * 32 + 16 * c2) * G::kRowBytes + a_vh[db];
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pr);
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pr + 8 * G::kRowBytes));
       // Join the two reads as one integer vector and reinterpret it whole: assembling the bf16
@@ -927,22 +941,23 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
   // then hold that piece's finite tiles)
   if (cur < kt_hi) issue(cur, 0);
   if (pc.first) {
-    constexpr int kPerWave = G::kStageBytes / 1024 / kWaves;  // 1 KB fetches per wave and stage
+    constexpr int kPerWave = G::kTileBytes / 1024 / kWaves;  // 1 KB fetches per wave and tile
     unsigned zoff[kPerWave];
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) zoff[j] = 0u;
 #pragma unroll
-    for (int st = 1; st < kStages; ++st)
+    for (int st = 1; st < kStages; ++st) {
       dma_rows<kPerWave>(reinterpret_cast<const void*>(p.q), 0,
-                         (lds_char*)lds_raw + st * G::kStageBytes + wave * kPerWave * 1024, zoff);
+                         (lds_char*)lds_raw + st * G::kTileBytes + wave * kPerWave * 1024, zoff);
+      dma_rows<kPerWave>(reinterpret_cast<const void*>(p.q), 0,
+                         (lds_char*)lds_raw + G::kVRegion + st * G::kTileBytes + wave * kPerWave * 1024, zoff);
+    }
   }
   if (cur < kt_hi) finish(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the zero fills have landed too
   __syncthreads();
-  int prv = kt_hi;
   TileView tv_cur{}, tv_prv{};
   tv_prv.live = false;
-  int st_cur = 0, st_prv = kStages - 1;
   auto softmax_phase = [&](const TileView& tv, int st) __attribute__((always_inline)) {
     if (__builtin_amdgcn_readfirstlane((int)tv.live)) {  // wave-uniform: a scalar branch
       softmax(tv, st);
@@ -960,14 +975,19 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
   // bias loads. Without a bias the shared loop is the faster one.)
   // One iteration; g1 / g2 (constants) say whether it has a current and a previous tile: the loop
   // runs one iteration without a previous tile, then full ones, then one without a current tile.
-  auto iteration = [&](auto group, auto g1, auto g2) __attribute__((always_inline)) {
+  // stage: the stage of the current tile (iteration k of a piece uses stage k mod 3), a constant in
+  // all but the last iteration (without a bias), so that the LDS addresses of the operand reads are
+  // constant offsets from the lane's read addresses.
+  auto iteration = [&](auto group, auto g1, auto g2, auto stage) __attribute__((always_inline)) {
     constexpr bool G1 = decltype(g1)::value;
     constexpr bool G2 = decltype(g2)::value;
     const bool GA = group;
+    const int st_cur = stage;
+    const int st_prv = st_cur == 0 ? kStages - 1 : st_cur - 1;
+    const int st_nxt = st_cur + 1 == kStages ? 0 : st_cur + 1;
     const int packed_nxt = next_tile(cur + 1 <= kt_hi ? cur + 1 : kt_hi);
     const int nxt = packed_nxt >> 1;
     const bool all_nxt = packed_nxt & 1;
-    const int st_nxt = st_cur + 1 == kStages ? 0 : st_cur + 1;
     if constexpr (G1) {
       tv_cur = view_of(cur, all_cur);
     } else {
@@ -988,8 +1008,10 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
       __builtin_amdgcn_s_waitcnt(0x0F70);  // V of tile cur has landed
     }
     // Nothing stored to LDS in the first half is read in the second (the K in flight targets
-    // the stage nobody reads this iteration), so the middle barrier only aligns the phases.
-    __builtin_amdgcn_s_barrier();
+    // the stage nobody reads this iteration), so the middle barrier only aligns the phases. At
+    // D = 128 without a bias the phases stay aligned by themselves and the iteration is faster
+    // without it; at D = 64 (a softmax phase much longer than the MFMA phase) it is faster with.
+    if constexpr (D != 128 || BIAS) __builtin_amdgcn_s_barrier();
     // second half
     if (GA) {
       if constexpr (G1) softmax_phase(tv_cur, st_cur);
@@ -1004,20 +1026,38 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
       }
     }
     lds_barrier();
-    prv = cur;
     tv_prv = tv_cur;
-    st_prv = st_cur;
     cur = nxt;
     all_cur = all_nxt;
-    st_cur = st_nxt;
   };
   auto main_loop = [&](auto group) __attribute__((always_inline)) {
     using T = std::true_type;
     using F = std::false_type;
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    static_assert(kStages == 3, "the loop is unrolled over three stages");
     if (cur < kt_hi) {
-      iteration(group, T{}, F{});
-      while (cur < kt_hi) iteration(group, T{}, T{});
-      iteration(group, F{}, T{});
+      iteration(group, T{}, F{}, S0{});
+      int st_last = 1;
+      if constexpr (!BIAS) {
+        for (;;) {
+          if (cur >= kt_hi) { st_last = 1; break; }
+          iteration(group, T{}, T{}, S1{});
+          if (cur >= kt_hi) { st_last = 2; break; }
+          iteration(group, T{}, T{}, S2{});
+          if (cur >= kt_hi) { st_last = 0; break; }
+          iteration(group, T{}, T{}, S0{});
+        }
+      } else {
+        // the bias mode runs a separate loop per wave group; unrolled, its bias loads in flight
+        // no longer fit the registers
+        while (cur < kt_hi) {
+          iteration(group, T{}, T{}, st_last);
+          st_last = st_last + 1 == kStages ? 0 : st_last + 1;
+        }
+      }
+      iteration(group, F{}, T{}, st_last);
     }
   };
   if constexpr (BIAS) {
