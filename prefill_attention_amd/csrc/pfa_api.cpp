@@ -318,12 +318,13 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int L, int S, int D) {
   // waves stream the keys fastest) at least twelve, which halves the partials the merge reads and
   // still leaves about 700 workgroups for one-token decode on a 32K cache (15 % faster per call
   // than four; the 64-row kernel needs the smaller splits to fill the chip); with two 32-row groups
-  // per KV head at least eight (measured on 56 rows of 8K keys per KV head: 22.4 us per call
-  // against 23.6 with twelve and 25.4 with four, whose partials the merge reads twice over)
+  // per KV head at least nine, a multiple of the kernel's three-tile step (measured on 56 rows of
+  // 8K keys per KV head: 18.2 us per call against 18.9 with eight, 19.3 with six and 19.8 with
+  // twelve)
   constexpr long long kTargetGroups = 1280;
   constexpr long long kMinTilesPerSplit = 4;
   constexpr long long kMinTilesPerSplitFewRows = 12;
-  constexpr long long kMinTilesPerSplitTwoGroups = 8;
+  constexpr long long kMinTilesPerSplitTwoGroups = 9;
   DecodePlan pl;
   const long long R = static_cast<long long>(Hq / Hkv) * L;
   // up to 64 rows per KV head go in groups of 32 (the one-block kernels, the register-K one
