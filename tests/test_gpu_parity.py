@@ -346,3 +346,23 @@ def test_binding_raises_status_errors():
     k = torch.zeros(1, 2, 8, 96, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(pfa.PfaError, match="PFA_ERR_HEAD_DIM"):
         pfa.prefill_attn_gqa(q, k, k)
+
+
+# ----------------------------------------------------------------------------------------------
+# The main loop runs its full iterations three to a round, one copy per LDS stage, and leaves
+# the round after any of them; the last iteration then runs on the stage it stopped at. Key-tile
+# counts 1 to 9 per query block (and a ragged last tile) take every exit, with and without a key
+# mask (the masked form reads the tile's mask bytes from the stage), at both head sizes.
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("n_tiles", list(range(1, 10)))
+def test_loop_exits_at_every_stage(D, n_tiles):
+    S = 64 * n_tiles - (0 if n_tiles % 2 else 17)
+    L = 40
+    mask = np.ones((1, S), dtype=np.uint8)
+    mask[0, 1::5] = 0
+    for m in (None, mask):
+        x = small_case(1, 4, 2, L, S, D, S - L, seed=70 + n_tiles, mask=m)
+        print(f"loop exits: D={D} tiles={n_tiles} S={S} key_mask={m is not None}", flush=True)
+        got = run(x)
+        check_close(to64(got), oracle_of(x), f"D={D} tiles={n_tiles} mask={m is not None}")
+        assert torch.equal(bits_of(got), bits_of(run(x, no_skip=True)))
