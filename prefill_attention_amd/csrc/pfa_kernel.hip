@@ -298,7 +298,6 @@ struct Piece {
   int item;
   int t_from, t_to, n;
   bool whole;
-  bool first;  // the workgroup's first piece: the LDS stages still have to be zeroed
   int slot;
   int v_first, n_parts;
 };
@@ -932,29 +931,16 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
   int packed = next_tile(kt_lo);
   int cur = packed >> 1;
   bool all_cur = packed & 1;
-  // The first tile goes to stage 0 (every byte of it written by the fetch); the other stages are
-  // zeroed once, so that a stage read before any tile lands there holds finite data. The zeroing
-  // is done by fetches from an empty buffer descriptor (they write zeros), issued behind the first
-  // tile's fetch so that both are in flight together.
+  // The first tile goes to stage 0 (every byte of it written by the fetch, keys past S as zeros).
+  // No GEMM ever reads a stage before its tile has landed: GEMM1 of an iteration reads the K of
+  // the tile fetched before it, GEMM2 the V of the tile fetched two halves earlier, and the first
+  // iteration of a piece runs no GEMM2. So the other stages need no initial contents (uninitialised
+  // LDS could hold non-finite bit patterns, which times P = 0 would still give NaN: the peeled
+  // first iteration is what keeps them out of the accumulators).
   // (a later piece of the workgroup reuses the stages: every wave has left the previous piece's
-  // loop, whose last barrier follows its last LDS read, before any wave gets here; the stages
-  // then hold that piece's finite tiles)
+  // loop, whose last barrier follows its last LDS read, before any wave gets here)
   if (cur < kt_hi) issue(cur, 0);
-  if (pc.first) {
-    constexpr int kPerWave = G::kTileBytes / 1024 / kWaves;  // 1 KB fetches per wave and tile
-    unsigned zoff[kPerWave];
-#pragma unroll
-    for (int j = 0; j < kPerWave; ++j) zoff[j] = 0u;
-#pragma unroll
-    for (int st = 1; st < kStages; ++st) {
-      dma_rows<kPerWave>(reinterpret_cast<const void*>(p.q), 0,
-                         (lds_char*)lds_raw + st * G::kTileBytes + wave * kPerWave * 1024, zoff);
-      dma_rows<kPerWave>(reinterpret_cast<const void*>(p.q), 0,
-                         (lds_char*)lds_raw + G::kVRegion + st * G::kTileBytes + wave * kPerWave * 1024, zoff);
-    }
-  }
   if (cur < kt_hi) finish(0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the zero fills have landed too
   __syncthreads();
   TileView tv_cur{}, tv_prv{};
   tv_prv.live = false;
@@ -1205,7 +1191,7 @@ __device__ __forceinline__ int split_wg_of(const SplitWalk& w, long long t) {
 }
 
 // The piece at w.pos (w.pos < w.r1), or done.
-__device__ __forceinline__ void split_piece(SplitWalk& w, bool first) {
+__device__ __forceinline__ void split_piece(SplitWalk& w) {
   if (w.pos >= w.r1) {
     w.done = 1;
     return;
@@ -1217,7 +1203,6 @@ __device__ __forceinline__ void split_piece(SplitWalk& w, bool first) {
   pc.t_from = (int)(w.pos - I);
   pc.t_to = (int)((w.r1 - I) < w.n ? (w.r1 - I) : w.n);
   pc.whole = pc.t_from == 0 && pc.t_to == w.n;
-  pc.first = first;
   pc.slot = part_slot(w.v, pc.t_from == 0);
   pc.v_first = pc.whole ? w.v : split_wg_of(w, I);
   pc.n_parts = pc.whole ? 1 : split_wg_of(w, I + w.n - 1) - pc.v_first + 1;
@@ -1259,7 +1244,7 @@ __device__ __forceinline__ void split_init(const Params& p, SplitWalk& w) {
   }
   w.in_block = rem / w.n;
   w.pos = r0;
-  split_piece(w, true);
+  split_piece(w);
 }
 
 __device__ __forceinline__ void split_next(const Params& p, SplitWalk& w) {
@@ -1272,7 +1257,7 @@ __device__ __forceinline__ void split_next(const Params& p, SplitWalk& w) {
     }
     w.n = split_tiles_of(p, w.qrank, w.nb);
   }
-  split_piece(w, false);
+  split_piece(w);
 }
 
 template <int D, int MODE, bool SPLIT>
@@ -1284,7 +1269,6 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
     Piece pc{};
     pc.item = item;
     pc.whole = true;
-    pc.first = true;
     prefill_piece<D, MODE>(p, pc, (int)threadIdx.x);
   } else {
     // key split (dense layout): a fixed grid, each workgroup its share of the linear space
@@ -1299,7 +1283,6 @@ __global__ __launch_bounds__(kThreads) void pfa_prefill_kernel(Params p) {
       pc.t_to = __builtin_amdgcn_readfirstlane(walk.pc.t_to);
       pc.n = __builtin_amdgcn_readfirstlane(walk.pc.n);
       pc.whole = __builtin_amdgcn_readfirstlane((int)walk.pc.whole) != 0;
-      pc.first = __builtin_amdgcn_readfirstlane((int)walk.pc.first) != 0;
       pc.slot = __builtin_amdgcn_readfirstlane(walk.pc.slot);
       pc.v_first = __builtin_amdgcn_readfirstlane(walk.pc.v_first);
       pc.n_parts = __builtin_amdgcn_readfirstlane(walk.pc.n_parts);
