@@ -21,8 +21,10 @@
 //  * Software pipeline and ping-pong: a wave's work on tile t is GEMM1(t) (scores), SOFTMAX(t)
 //    and GEMM2(t) (P.V). A wave runs "GEMM1(t) + GEMM2(t-1)" as one MFMA phase and SOFTMAX(t) as
 //    one VALU phase. Waves 0-3 and 4-7 run these phases in opposite halves of each iteration
-//    (two barriers per iteration), so on every SIMD one wave feeds the matrix core while the
-//    other runs the exponentials. In the MFMA phase each LDS operand is read three MFMAs ahead.
+//    (a barrier closes each iteration; one between the halves at D = 64 and with a bias), so on
+//    every SIMD one wave feeds the matrix core while the other runs the exponentials. In the MFMA
+//    phase each LDS operand is read three MFMAs ahead, at an immediate offset: the loop is unrolled
+//    once per LDS stage.
 //  * K/V tiles (64 keys x D) go from HBM straight into LDS with buffer_load_dwordx4 ... lds (each
 //    instruction writes 1 KB of consecutive LDS; waves 0-3 fetch K, waves 4-7 fetch V), into one
 //    of three stages: tile t+1 lands while tile t's K and tile t-1's V are read. Rows are
@@ -920,10 +922,11 @@ __device__ __forceinline__ void prefill_piece(const Params& p, const Piece& pc, 
 
   // ---- main loop ----
   // An iteration works on tile `cur` (its K in stage st_cur), tile `prv` (its V in stage st_prv)
-  // and fetches tile `nxt` into the third stage. Each half of an iteration ends with a barrier;
-  // a wave runs its MFMA phase in one half and its softmax phase in the other (group A: MFMA
-  // first). Group A issues the fetch of `nxt` right after its MFMA phase; it lands during the
-  // second half and is waited for before the closing barrier.
+  // and fetches tile `nxt` into the third stage. A wave runs its MFMA phase in one half of the
+  // iteration and its softmax phase in the other (group A: MFMA first); the iteration ends with a
+  // barrier (and, at D = 64 or with a bias, its halves are separated by one). Group A issues the
+  // fetch of `nxt` right after its MFMA phase; it lands during the second half and is waited for
+  // before the closing barrier.
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
